@@ -1,0 +1,11 @@
+"""fp64 CPU oracle for DiffQKV attention -- test infrastructure only.
+
+Imported by the test-suite, the smoke check and the benchmark's CPU-baseline
+leg; never by the GPU library.
+"""
+
+from .attention import (attend_one, attention_weights, decode, default_scale,
+                        group_sharing_index, kv_append, prefill)
+
+__all__ = ["attend_one", "attention_weights", "decode", "default_scale",
+           "group_sharing_index", "kv_append", "prefill"]

@@ -1,0 +1,162 @@
+"""fp64 CPU oracle for DiffQKV attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  The GPU library never calls it and it never calls the GPU
+library: the two share no code.
+
+This is the plain definition of the attention that the Sigma pages describe,
+written for a reader to check against them by eye.  Citations name the page
+("Sigma architecture page" = the paper-graph-ui.vercel.app architecture
+summary of arXiv 2501.13629 "Sigma: Differential Rescaling of Query, Key and
+Value for Efficient Language Models"; "Pith review page" = pith.science's
+review of the same paper) and the section or equation on it.
+
+Everything is computed in float64 from inputs widened exactly from their
+storage type.  The softmax is two-pass (maximum, then normalised exponentials)
+and unchunked: it deliberately shares no structure with the split/online GPU
+kernels.  numpy's matrix-vector product is the only library step.
+
+Readings taken where the pages are silent (all listed in the design doc):
+* scale defaults to 1/sqrt(d_k)                (architecture page, §3.4 Step 4)
+* head maps are floor(i * n_h / n_q), 0-based  (§3.4 Step 3; FlexHeadFA section)
+* the newest token attends to itself: ctx_len counts the rows after the
+  append of Step 2                              (§3.4 Steps 2 and 5)
+* prefill rows use a bottom-right causal mask: new row r of a sequence with
+  L rows attends keys 0 .. L - t_new + r       (not on the pages)
+* an empty context yields o = 0, lse = -inf    (never arises in a decoder)
+
+Pins (tests/test_oracle.py): the FlexHeadFA index worked example, reduction
+to textbook MHA / GQA / MQA (torch's scaled_dot_product_attention in fp64),
+weights summing to 1, brute-force softmax without max-shift on tiny shapes,
+the kv_group_sharing equivalence, closed forms (one key, zero scale, two keys
+with chosen logits), key-permutation invariance, prefill/decode consistency
+and causal masking, and Step 2's concatenation for the append.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def group_sharing_index(i: int, n_q: int, n_h: int) -> int:
+    """Index of the K (or V) head that query head ``i`` reads.
+
+    Sigma architecture page, §3.4 Step 3 (GroupSharing): query head i uses
+    head floor(i * n_h / n_q); the FlexHeadFA section gives the same address
+    rule idx_h = idx_q * n_h / n_q with 0-based indices (query heads 0 and 1
+    read K head 0 and V head 0, query head 2 reads V head 1, for 32/4/16).
+    """
+    return (int(i) * int(n_h)) // int(n_q)
+
+
+def default_scale(d_k: int) -> float:
+    """1/sqrt(d_k): the divisor of the Attend scores in §3.4 Step 4."""
+    return 1.0 / math.sqrt(d_k)
+
+
+def attention_weights(q_i: np.ndarray, K_i: np.ndarray, scale: float):
+    """alpha = Softmax(scale * Attend(q_i, K_i)) and its log-sum-exp.
+
+    §3.4 Step 4: Attend is the inner product of the d_k-dimensional query head
+    with every key row.  Two passes: the largest score, then exponentials of
+    the shifted scores normalised by their sum (subtracting a constant leaves
+    the softmax unchanged in exact arithmetic).
+
+    Returns ``(alpha[L], lse)`` with ``lse = log(sum_j exp(scale * q.k_j))``.
+    """
+    q64 = np.asarray(q_i, dtype=np.float64)
+    K64 = np.asarray(K_i, dtype=np.float64)
+    s = scale * (K64 @ q64)
+    m = s.max()
+    w = np.exp(s - m)
+    z = w.sum()
+    return w / z, float(m + math.log(z))
+
+
+def attend_one(q_i, K_i, V_i, scale: float):
+    """o = sum_j alpha_j V_j for one query head (§3.4 Step 5)."""
+    if K_i.shape[0] == 0:
+        return np.zeros(V_i.shape[1], dtype=np.float64), -math.inf
+    alpha, lse = attention_weights(q_i, K_i, scale)
+    return alpha @ np.asarray(V_i, dtype=np.float64), lse
+
+
+def decode(q, k_cache, v_cache, ctx_len, scale: float | None = None):
+    """One decode step of DiffQKV attention.
+
+    Shapes: ``q[B][n_q][d_k]``, ``k_cache[B][n_k][l_cap][d_k]``,
+    ``v_cache[B][n_v][l_cap][d_v]``, ``ctx_len[B]`` (rows attended, newest
+    included).  Query head i of sequence b attends rows 0..L_b-1 of K head
+    floor(i*n_k/n_q) and weights rows of V head floor(i*n_v/n_q)
+    (§3.4 Steps 3-5).  Returns ``(out[B][n_q][d_v], lse[B][n_q])`` in float64.
+    """
+    B, n_q, d_k = q.shape
+    n_k = k_cache.shape[1]
+    n_v, d_v = v_cache.shape[1], v_cache.shape[3]
+    if scale is None:
+        scale = default_scale(d_k)
+    out = np.zeros((B, n_q, d_v), dtype=np.float64)
+    lse = np.full((B, n_q), -math.inf, dtype=np.float64)
+    for b in range(B):
+        L = int(ctx_len[b])
+        for i in range(n_q):
+            g = group_sharing_index(i, n_q, n_k)
+            hv = group_sharing_index(i, n_q, n_v)
+            out[b, i], lse[b, i] = attend_one(q[b, i], k_cache[b, g, :L],
+                                              v_cache[b, hv, :L], scale)
+    return out, lse
+
+
+def prefill(q, k_cache, v_cache, ctx_len, scale: float | None = None,
+            rows=None):
+    """Causal attention of ``t_new`` new query rows against the cache.
+
+    ``q[B][t_new][n_q][d_k]``; ``ctx_len[B]`` counts cache rows *after* the
+    new rows were appended (so ``ctx_len[b] >= t_new``).  New row r of
+    sequence b sits at position p = ctx_len[b] - t_new + r and attends keys
+    0..p: each token attends every earlier token and itself (§3.4 Steps 2 and
+    5, applied token by token).
+
+    ``rows`` optionally restricts the computation to a list of ``(b, r)``;
+    the other rows are returned as NaN.  Returns ``(out[B][t_new][n_q][d_v],
+    lse[B][t_new][n_q])`` in float64.
+    """
+    B, T, n_q, d_k = q.shape
+    n_k = k_cache.shape[1]
+    n_v, d_v = v_cache.shape[1], v_cache.shape[3]
+    if scale is None:
+        scale = default_scale(d_k)
+    if rows is None:
+        rows = [(b, r) for b in range(B) for r in range(T)]
+    out = np.full((B, T, n_q, d_v), np.nan, dtype=np.float64)
+    lse = np.full((B, T, n_q), np.nan, dtype=np.float64)
+    for b, r in rows:
+        p = int(ctx_len[b]) - T + r
+        for i in range(n_q):
+            g = group_sharing_index(i, n_q, n_k)
+            hv = group_sharing_index(i, n_q, n_v)
+            out[b, r, i], lse[b, r, i] = attend_one(
+                q[b, r, i], k_cache[b, g, :p + 1], v_cache[b, hv, :p + 1], scale)
+    return out, lse
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, pos):
+    """Step 2 of §3.4: K_t = [K_{t-1}; k_t], V_t = [V_{t-1}; v_t].
+
+    The K and V caches are separate arrays with their own head counts and
+    head dimensions (architecture page §3.2 item 3).  ``k_new[B][T][n_k][d_k]``
+    and ``v_new[B][T][n_v][d_v]`` are token-major; token t of sequence b is
+    written at cache row ``pos[b] + t`` of every head.  Works on raw storage
+    (bf16 bit patterns or float32) and returns new arrays; a pure copy.
+    """
+    k = np.array(k_cache, copy=True)
+    v = np.array(v_cache, copy=True)
+    B, T = k_new.shape[0], k_new.shape[1]
+    for b in range(B):
+        for t in range(T):
+            row = int(pos[b]) + t
+            k[b, :, row, :] = k_new[b, t]
+            v[b, :, row, :] = v_new[b, t]
+    return k, v
