@@ -1,0 +1,208 @@
+"""DiffQKV attention on AMD MI355X: Python binding of libdiffqkv.so.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream.  The C ABI and its
+contracts are documented in ``include/diffqkv.h``.
+
+Tensor layouts (contiguous, on one GPU):
+  q (decode)   [B, n_q, d_k]            q (prefill)  [B, t_new, n_q, d_k]
+  k_cache      [B, n_k, l_cap, d_k]     v_cache      [B, n_v, l_cap, d_v]
+  k_new        [B, t_new, n_k, d_k]     v_new        [B, t_new, n_v, d_v]
+  ctx_len, pos int32 [B]
+dtype float32 or bfloat16 (prefill: bfloat16).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["DQKVError", "lib_path", "load", "decode", "decode_chunk",
+           "decode_workspace_bytes", "prefill", "kv_append", "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libdiffqkv.so")
+
+STATUS = {0: "DQKV_OK", -1: "DQKV_ERR_NULL", -2: "DQKV_ERR_SHAPE",
+          -3: "DQKV_ERR_UNSUPPORTED", -4: "DQKV_ERR_WORKSPACE",
+          -5: "DQKV_ERR_HIP", -6: "DQKV_ERR_ALIGN"}
+F32, BF16 = 0, 1
+
+_i32, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+# Exported symbols and their C signatures (include/diffqkv.h).
+SIGNATURES = {
+    "dqkv_status_str": (ctypes.c_char_p, [_i32]),
+    "diffqkv_decode_chunk": (_i32, [_i32] * 7 + [ctypes.POINTER(_i32)]),
+    "diffqkv_decode_workspace": (_i32, [_i32] * 8 + [ctypes.POINTER(_sz)]),
+    "kv_append": (_i32, [_i32] * 9 + [_vp] * 6),
+    "diffqkv_decode": (_i32, [_i32] * 9 + [_f32] + [_vp] * 6 + [_i32, _vp, _sz, _vp]),
+    "diffqkv_prefill": (_i32, [_i32] * 9 + [_f32] + [_vp] * 7),
+    "diffqkv_decode_split": (_i32, [_i32] * 9 + [_f32] + [_vp] * 4 + [_i32, _vp, _sz, _vp]),
+    "diffqkv_decode_combine": (_i32, [_i32] * 9 + [_vp] * 3 + [_i32, _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+class DQKVError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_str(status)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libdiffqkv.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(
+                f"{lib_path} is missing: build it with "
+                "`python -m asymmetric_head_kv_amd.build` (or __graft_entry__.build())")
+        lib = ctypes.CDLL(lib_path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return load().dqkv_status_str(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise DQKVError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _device_tensors(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def decode_chunk(n_q, n_k, n_v, d_k, d_v, batch, max_ctx) -> int:
+    """Rows per context chunk that diffqkv_decode picks automatically."""
+    out = _i32()
+    _check("diffqkv_decode_chunk",
+           load().diffqkv_decode_chunk(n_q, n_k, n_v, d_k, d_v, batch, max_ctx,
+                                       ctypes.byref(out)))
+    return out.value
+
+
+def decode_workspace_bytes(n_q, n_k, n_v, d_k, d_v, batch, max_ctx,
+                           chunk_tokens: int = 0) -> int:
+    out = _sz()
+    _check("diffqkv_decode_workspace",
+           load().diffqkv_decode_workspace(n_q, n_k, n_v, d_k, d_v, batch, max_ctx,
+                                           chunk_tokens, ctypes.byref(out)))
+    return out.value
+
+
+def kv_append(k_new, v_new, pos, k_cache, v_cache, *, n_q=None, stream=None):
+    """Write token-major rows k_new/v_new into the caches at rows pos[b] + t."""
+    _device_tensors(k_new, v_new, pos, k_cache, v_cache)
+    B, T, n_k, d_k = k_new.shape
+    n_v, d_v = v_new.shape[2], v_new.shape[3]
+    if k_cache.shape[:2] != (B, n_k) or v_cache.shape[:2] != (B, n_v) or \
+            k_cache.shape[3] != d_k or v_cache.shape[3] != d_v or \
+            v_cache.shape[2] != k_cache.shape[2] or v_new.shape[:2] != (B, T):
+        raise ValueError("inconsistent cache / new-row shapes")
+    if pos.dtype != torch.int32 or pos.numel() != B:
+        raise ValueError("pos must be int32 [B]")
+    for t in (v_new, k_cache, v_cache):
+        if t.dtype != k_new.dtype:
+            raise TypeError("k_new, v_new and the caches must share one dtype")
+    n_q = max(n_k, n_v) if n_q is None else n_q
+    _check("kv_append", load().kv_append(
+        n_q, n_k, n_v, d_k, d_v, _dtype_code(k_new), B, T, k_cache.shape[2],
+        _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(k_cache), _ptr(v_cache), _stream(stream)))
+
+
+def decode(q, k_cache, v_cache, ctx_len, *, max_ctx=None, scale=None, out=None,
+           lse=None, chunk_tokens=0, workspace=None, stream=None):
+    """One decode step; returns (out [B, n_q, d_v], lse [B, n_q] or None)."""
+    _device_tensors(q, k_cache, v_cache, ctx_len, out, lse, workspace)
+    B, n_q, d_k = q.shape
+    n_k, l_cap = k_cache.shape[1], k_cache.shape[2]
+    n_v, d_v = v_cache.shape[1], v_cache.shape[3]
+    if k_cache.shape != (B, n_k, l_cap, d_k) or v_cache.shape[:3] != (B, n_v, l_cap):
+        raise ValueError("inconsistent q / cache shapes")
+    if ctx_len.dtype != torch.int32 or ctx_len.numel() != B:
+        raise ValueError("ctx_len must be int32 [B]")
+    for t in (k_cache, v_cache):
+        if t.dtype != q.dtype:
+            raise TypeError("q and the caches must share one dtype")
+    max_ctx = l_cap if max_ctx is None else int(max_ctx)
+    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, n_q, d_v), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, n_q, d_v) or out.dtype != q.dtype:
+        raise ValueError("out must be [B, n_q, d_v] in q's dtype")
+    if lse is not None and (lse.shape != (B, n_q) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, n_q]")
+    need = decode_workspace_bytes(n_q, n_k, n_v, d_k, d_v, B, max_ctx, chunk_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("diffqkv_decode", load().diffqkv_decode(
+        n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, l_cap, max_ctx, scale,
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(out), _ptr(lse),
+        int(chunk_tokens), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out, lse
+
+
+def prefill(q, k_cache, v_cache, ctx_len, *, scale=None, out=None, lse=None,
+            stream=None):
+    """Causal prefill of t_new rows (already appended); returns (out, lse)."""
+    _device_tensors(q, k_cache, v_cache, ctx_len, out, lse)
+    B, T, n_q, d_k = q.shape
+    n_k, l_cap = k_cache.shape[1], k_cache.shape[2]
+    n_v, d_v = v_cache.shape[1], v_cache.shape[3]
+    if k_cache.shape != (B, n_k, l_cap, d_k) or v_cache.shape[:3] != (B, n_v, l_cap):
+        raise ValueError("inconsistent q / cache shapes")
+    if ctx_len.dtype != torch.int32 or ctx_len.numel() != B:
+        raise ValueError("ctx_len must be int32 [B]")
+    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, T, n_q, d_v), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, T, n_q, d_v) or out.dtype != q.dtype:
+        raise ValueError("out must be [B, t_new, n_q, d_v] in q's dtype")
+    if lse is not None and (lse.shape != (B, T, n_q) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, t_new, n_q]")
+    _check("diffqkv_prefill", load().diffqkv_prefill(
+        n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, T, l_cap, scale,
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(out), _ptr(lse),
+        _stream(stream)))
+    return out, lse

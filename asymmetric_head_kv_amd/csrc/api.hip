@@ -1,0 +1,259 @@
+// C ABI of the DiffQKV attention library (declarations and contracts in
+// include/diffqkv.h): argument validation, launch planning and workspace
+// layout.  No entry point allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "diffqkv.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kCUs = 256;             // MI355X compute units
+constexpr int kWavesPerCUTarget = 8;  // split waves to aim for per CU
+constexpr int kMaxChunks = 8192;      // combine keeps one weight per chunk in LDS
+constexpr int kMinChunk = 64;
+
+bool is_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+int check_heads(int n_q, int n_k, int n_v, int d_k, int d_v) {
+  if (n_q <= 0 || n_k <= 0 || n_v <= 0 || d_k <= 0 || d_v <= 0) return DQKV_ERR_SHAPE;
+  if (n_k > n_q || n_v > n_q || n_q % n_k != 0 || n_q % n_v != 0) return DQKV_ERR_SHAPE;
+  return DQKV_OK;
+}
+
+int check_dtype_dims(int dtype, int d_k, int d_v) {
+  if (dtype != DQKV_F32 && dtype != DQKV_BF16) return DQKV_ERR_UNSUPPORTED;
+  if (!is_dim(d_k) || !is_dim(d_v)) return DQKV_ERR_UNSUPPORTED;
+  if (dtype == DQKV_F32 && d_k == 256) return DQKV_ERR_UNSUPPORTED;
+  return DQKV_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int to_status(hipError_t e) { return e == hipSuccess ? DQKV_OK : DQKV_ERR_HIP; }
+
+// Rows per context chunk: enough (sequence, head-quad, chunk) workgroups to
+// give every CU about kWavesPerCUTarget waves, in multiples of 64 rows.
+int plan_chunk(int n_q, int batch, int max_ctx) {
+  const long long quads = (long long)batch * ((n_q + 3) / 4);
+  const long long want_wg = (long long)kCUs * kWavesPerCUTarget / 4;
+  long long chunks_per_seq = (want_wg + quads - 1) / quads;
+  if (chunks_per_seq < 1) chunks_per_seq = 1;
+  long long S = (max_ctx + chunks_per_seq - 1) / chunks_per_seq;
+  S = (S + kMinChunk - 1) / kMinChunk * kMinChunk;
+  if (S < kMinChunk) S = kMinChunk;
+  const long long s_floor = ((long long)max_ctx + kMaxChunks - 1) / kMaxChunks;
+  if (S < s_floor) S = (s_floor + kMinChunk - 1) / kMinChunk * kMinChunk;
+  if (S > (1 << 30)) S = 1 << 30;
+  return (int)S;
+}
+
+int chunks_for(int max_ctx, int S) {
+  const int c = (int)(((long long)max_ctx + S - 1) / S);
+  return c < 1 ? 1 : c;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(int n_q, int d_v, int batch, int C) {
+  const size_t parts = (size_t)batch * n_q * C;
+  return align256(parts * 2 * sizeof(float)) + parts * d_v * sizeof(float);
+}
+
+int resolve_chunk(int n_q, int batch, int max_ctx, int chunk_tokens, int* S) {
+  if (chunk_tokens < 0 || chunk_tokens % kMinChunk != 0) return DQKV_ERR_SHAPE;
+  *S = chunk_tokens ? chunk_tokens : plan_chunk(n_q, batch, max_ctx);
+  if (chunks_for(max_ctx, *S) > kMaxChunks) return DQKV_ERR_UNSUPPORTED;
+  return DQKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dqkv_status_str(int32_t status) {
+  switch (status) {
+    case DQKV_OK: return "DQKV_OK";
+    case DQKV_ERR_NULL: return "DQKV_ERR_NULL: a required pointer is NULL";
+    case DQKV_ERR_SHAPE: return "DQKV_ERR_SHAPE: sizes violate the head / length rules";
+    case DQKV_ERR_UNSUPPORTED: return "DQKV_ERR_UNSUPPORTED: size or dtype not built";
+    case DQKV_ERR_WORKSPACE: return "DQKV_ERR_WORKSPACE: workspace too small";
+    case DQKV_ERR_HIP: return "DQKV_ERR_HIP: the HIP runtime refused a launch";
+    case DQKV_ERR_ALIGN: return "DQKV_ERR_ALIGN: a device pointer is not 16-byte aligned";
+  }
+  return "unknown dqkv status";
+}
+
+int32_t diffqkv_decode_chunk(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                             int32_t d_v, int32_t batch, int32_t max_ctx,
+                             int32_t* chunk_tokens) {
+  if (!chunk_tokens) return DQKV_ERR_NULL;
+  int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+  if (st) return st;
+  if (batch < 0 || max_ctx < 0) return DQKV_ERR_SHAPE;
+  return resolve_chunk(n_q, batch, max_ctx, 0, chunk_tokens);
+}
+
+int32_t diffqkv_decode_workspace(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                                 int32_t d_v, int32_t batch, int32_t max_ctx,
+                                 int32_t chunk_tokens, size_t* bytes) {
+  if (!bytes) return DQKV_ERR_NULL;
+  int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+  if (st) return st;
+  if (batch < 0 || max_ctx < 0) return DQKV_ERR_SHAPE;
+  int S = 0;
+  st = resolve_chunk(n_q, batch, max_ctx, chunk_tokens, &S);
+  if (st) return st;
+  *bytes = workspace_bytes(n_q, d_v, batch, chunks_for(max_ctx, S));
+  return DQKV_OK;
+}
+
+int32_t kv_append(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                  int32_t dtype, int32_t batch, int32_t t_new, int32_t l_cap,
+                  const void* k_new, const void* v_new, const int32_t* pos,
+                  void* k_cache, void* v_cache, void* stream) {
+  int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+  if (st) return st;
+  st = check_dtype_dims(dtype, d_k, d_v);
+  if (st) return st;
+  if (batch < 0 || t_new < 0 || l_cap < 0 || batch > 65535) return DQKV_ERR_SHAPE;
+  if (batch == 0 || t_new == 0) return DQKV_OK;
+  if (!k_new || !v_new || !pos || !k_cache || !v_cache) return DQKV_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return DQKV_ERR_ALIGN;
+  dqkv::AppendArgs a;
+  a.elem_bytes = dtype == DQKV_BF16 ? 2 : 4;
+  a.n_k = n_k; a.n_v = n_v; a.d_k = d_k; a.d_v = d_v;
+  a.batch = batch; a.t_new = t_new; a.l_cap = l_cap;
+  a.k_new = k_new; a.v_new = v_new; a.pos = pos;
+  a.k_cache = k_cache; a.v_cache = v_cache;
+  a.stream = (hipStream_t)stream;
+  return to_status(dqkv::launch_kv_append(a));
+}
+
+// Validates a decode call and fills the launch descriptor.  need_qkv /
+// need_out select which buffers the caller's entry point uses.
+static int prepare_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                          int32_t dtype, int32_t batch, int32_t l_cap, int32_t max_ctx,
+                          float scale, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* ctx_len, void* out,
+                          float* lse, int32_t chunk_tokens, void* workspace,
+                          size_t workspace_bytes_given, void* stream, bool need_qkv,
+                          bool need_out, dqkv::DecodeArgs* a) {
+  int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+  if (st) return st;
+  st = check_dtype_dims(dtype, d_k, d_v);
+  if (st) return st;
+  if (batch < 0 || l_cap < 0 || max_ctx < 0 || max_ctx > l_cap || batch > 65535)
+    return DQKV_ERR_SHAPE;
+  if (need_qkv && (!(scale > 0.f) || !isfinite(scale))) return DQKV_ERR_SHAPE;
+  if (need_qkv && (!q || !k_cache || !v_cache)) return DQKV_ERR_NULL;
+  if (need_out && !out) return DQKV_ERR_NULL;
+  if (!ctx_len || !workspace) return DQKV_ERR_NULL;
+  if ((need_qkv && (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))) ||
+      (need_out && !aligned16(out)) || !aligned16(workspace))
+    return DQKV_ERR_ALIGN;
+  int S = 0;
+  st = resolve_chunk(n_q, batch, max_ctx, chunk_tokens, &S);
+  if (st) return st;
+  const int C = chunks_for(max_ctx, S);
+  if ((long long)(n_q + 3) / 4 > 65535) return DQKV_ERR_UNSUPPORTED;
+  const size_t need = workspace_bytes(n_q, d_v, batch, C);
+  if (workspace_bytes_given < need) return DQKV_ERR_WORKSPACE;
+
+  a->bf16 = dtype == DQKV_BF16;
+  a->n_q = n_q; a->n_k = n_k; a->n_v = n_v; a->d_k = d_k; a->d_v = d_v;
+  a->batch = batch; a->l_cap = l_cap; a->max_ctx = max_ctx;
+  a->S = S; a->C = C; a->scale = scale;
+  a->q = q; a->k_cache = k_cache; a->v_cache = v_cache; a->ctx_len = ctx_len;
+  a->out = out; a->lse = lse;
+  const size_t parts = (size_t)batch * n_q * C;
+  a->part_ml = (float*)workspace;
+  a->part_acc = (float*)((char*)workspace + align256(parts * 2 * sizeof(float)));
+  a->stream = (hipStream_t)stream;
+  return DQKV_OK;
+}
+
+int32_t diffqkv_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                       int32_t dtype, int32_t batch, int32_t l_cap, int32_t max_ctx,
+                       float scale, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* ctx_len, void* out,
+                       float* lse, int32_t chunk_tokens, void* workspace,
+                       size_t workspace_bytes_given, void* stream) {
+  if (batch == 0 && n_q > 0) {
+    int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+    return st ? st : check_dtype_dims(dtype, d_k, d_v);
+  }
+  dqkv::DecodeArgs a;
+  int st = prepare_decode(n_q, n_k, n_v, d_k, d_v, dtype, batch, l_cap, max_ctx, scale, q,
+                          k_cache, v_cache, ctx_len, out, lse, chunk_tokens, workspace,
+                          workspace_bytes_given, stream, true, true, &a);
+  if (st) return st;
+  st = to_status(dqkv::launch_decode_split(a));
+  if (st) return st;
+  return to_status(dqkv::launch_decode_combine(a));
+}
+
+int32_t diffqkv_decode_split(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                             int32_t dtype, int32_t batch, int32_t l_cap, int32_t max_ctx,
+                             float scale, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* ctx_len,
+                             int32_t chunk_tokens, void* workspace,
+                             size_t workspace_bytes_given, void* stream) {
+  if (batch == 0 && n_q > 0) {
+    int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+    return st ? st : check_dtype_dims(dtype, d_k, d_v);
+  }
+  dqkv::DecodeArgs a;
+  int st = prepare_decode(n_q, n_k, n_v, d_k, d_v, dtype, batch, l_cap, max_ctx, scale, q,
+                          k_cache, v_cache, ctx_len, nullptr, nullptr, chunk_tokens,
+                          workspace, workspace_bytes_given, stream, true, false, &a);
+  if (st) return st;
+  return to_status(dqkv::launch_decode_split(a));
+}
+
+int32_t diffqkv_decode_combine(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                               int32_t d_v, int32_t dtype, int32_t batch, int32_t l_cap,
+                               int32_t max_ctx, const int32_t* ctx_len, void* out,
+                               float* lse, int32_t chunk_tokens, void* workspace,
+                               size_t workspace_bytes_given, void* stream) {
+  if (batch == 0 && n_q > 0) {
+    int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+    return st ? st : check_dtype_dims(dtype, d_k, d_v);
+  }
+  dqkv::DecodeArgs a;
+  int st = prepare_decode(n_q, n_k, n_v, d_k, d_v, dtype, batch, l_cap, max_ctx, 1.f,
+                          nullptr, nullptr, nullptr, ctx_len, out, lse, chunk_tokens,
+                          workspace, workspace_bytes_given, stream, false, true, &a);
+  if (st) return st;
+  return to_status(dqkv::launch_decode_combine(a));
+}
+
+int32_t diffqkv_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                        int32_t dtype, int32_t batch, int32_t t_new, int32_t l_cap,
+                        float scale, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* ctx_len, void* out,
+                        float* lse, void* stream) {
+  int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+  if (st) return st;
+  if (dtype != DQKV_BF16) return DQKV_ERR_UNSUPPORTED;
+  if ((d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128)) return DQKV_ERR_UNSUPPORTED;
+  if (batch < 0 || t_new < 0 || l_cap < 0 || batch > 65535) return DQKV_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return DQKV_ERR_SHAPE;
+  if (batch == 0 || t_new == 0) return DQKV_OK;
+  if (!q || !k_cache || !v_cache || !ctx_len || !out) return DQKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return DQKV_ERR_ALIGN;
+  dqkv::PrefillArgs a;
+  a.n_q = n_q; a.n_k = n_k; a.n_v = n_v; a.d_k = d_k; a.d_v = d_v;
+  a.batch = batch; a.t_new = t_new; a.l_cap = l_cap; a.scale = scale;
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.ctx_len = ctx_len;
+  a.out = out; a.lse = lse;
+  a.stream = (hipStream_t)stream;
+  return to_status(dqkv::launch_prefill(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,310 @@
+// Split-KV decode attention with asymmetric K / V heads, and the exact
+// log-sum-exp combine of its per-chunk partial results.
+//
+// Computes, for every sequence b and query head i (Sigma architecture page,
+// section 3.4 Steps 3-5; FlexHeadFA section for the split/combine structure):
+//   s_j = scale * q_i . K[floor(i n_k / n_q)][j],     j < ctx_len[b]
+//   o_i = sum_j softmax(s)_j V[floor(i n_v / n_q)][j]
+//
+// Split kernel: one wavefront per (sequence, query head, context chunk); a
+// workgroup holds the four consecutive query heads of one chunk, so when
+// n_q / n_k >= 4 its four waves read the same K rows (the first wave to touch
+// a row brings it from HBM, the others hit the CU's L1 / the XCD's L2).  Each
+// wave walks its chunk in tiles of 64 rows:
+//   * all K and V loads of the tile are issued at once (16-byte lane loads,
+//     1 KiB contiguous per wave instruction);
+//   * scores: each lane multiplies its 16-byte slice of a K row with the
+//     matching slice of q, DPP sums over the lanes of a row; each lane keeps
+//     the score of exactly one row of the tile;
+//   * online softmax over tiles (running max m, running sum l, rescaled
+//     accumulator), max / sum by wave reductions, base-2 exponentials with
+//     log2(e) folded into the query scale;
+//   * V rows are accumulated in fp32 with each lane owning a 16-byte column
+//     slice; the row's probability arrives by ds_bpermute from the lane that
+//     owns it.
+// The chunk's (m, l, acc[d_v]) goes to the workspace.
+//
+// Combine kernel: one workgroup per (sequence, query head) merges the chunks
+//   M = max_c m_c, w_c = 2^(m_c - M), Lambda = sum_c w_c l_c,
+//   o = sum_c w_c acc_c / Lambda, lse = (M + log2 Lambda) ln 2,
+// which is exact in real arithmetic.  Chunks past the sequence's length are
+// never read.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace dqkv {
+
+constexpr int kTile = 64;  // rows per wave iteration: one score per lane
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const int32_t* __restrict__ ctx_len, float* __restrict__ part_ml,
+    float* __restrict__ part_acc, int n_q, int n_k, int n_v, int l_cap,
+    int max_ctx, int S, int C, float qscale) {
+  constexpr int EPL = Elem<T>::kPer16;       // elements per 16-byte lane load
+  constexpr int LPR_K = DK / EPL;            // lanes per K row
+  constexpr int RPL_K = 64 / LPR_K;          // K rows per wave load
+  constexpr int NK = kTile / RPL_K;          // K wave loads per tile (= LPR_K)
+  constexpr int LPR_V = DV / EPL;            // lanes per V row
+  constexpr int RPL_V = 64 / LPR_V;          // V rows per wave load
+  constexpr int NV = kTile / RPL_V;          // V wave loads per tile
+  constexpr int VB = NV < 16 ? NV : 16;      // V loads held in registers at once
+  static_assert(LPR_K >= 1 && LPR_K <= 32 && LPR_V >= 1 && LPR_V <= 64, "head dim");
+
+  const int c = blockIdx.x, quad = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = quad * 4 + wave;
+  if (i >= n_q) return;
+  int L = ctx_len[b];
+  L = max(0, min(L, min(max_ctx, l_cap)));
+  const int j0 = c * S;
+  if (j0 >= L) return;
+  const int rows = min(S, L - j0);
+  const int hk = (i * n_k) / n_q;
+  const int hv = (i * n_v) / n_q;
+
+  // This lane's slice of q (scaled by scale * log2 e).
+  const int kl = lane % LPR_K, kr = lane / LPR_K;
+  float qf[EPL];
+  Elem<T>::unpack(load16(q + ((size_t)b * n_q + i) * DK + kl * EPL), qf);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qf[e] *= qscale;
+
+  const T* kp = kc + (((size_t)b * n_k + hk) * l_cap + j0) * DK + kl * EPL;
+  const int vl = lane % LPR_V, vr = lane / LPR_V;
+  const T* vp = vc + (((size_t)b * n_v + hv) * l_cap + j0) * DV + vl * EPL;
+
+  // The lane keeps the score of tile row my_row = kl * RPL_K + kr (K load kl,
+  // row kr of that load); row r's score therefore sits in lane
+  // (r % RPL_K) * LPR_K + r / RPL_K.
+  const int my_row = kl * RPL_K + kr;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+
+  for (int t0 = 0; t0 < rows; t0 += kTile) {
+    // Issue the tile's K loads and the first VB V loads together.
+    u32x4 kv[NK], vv[VB];
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int r = t0 + u * RPL_K + kr;
+      kv[u] = r < rows ? load16(kp + (size_t)r * DK) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < VB; ++u) {
+      const int r = t0 + u * RPL_V + vr;
+      vv[u] = r < rows ? load16(vp + (size_t)r * DV) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    float s_mine = 0.f;
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      float kf[EPL];
+      Elem<T>::unpack(kv[u], kf);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s = fmaf(qf[e], kf[e], s);
+      s = group_sum<LPR_K>(s);
+      s_mine = (u == kl) ? s : s_mine;
+    }
+    if (t0 + my_row >= rows) s_mine = -INFINITY;
+
+    const float m_new = fmaxf(m_run, wave_max(s_mine));
+    const float p = fast_exp2(s_mine - m_new);
+    const float alpha = fast_exp2(m_run - m_new);
+    l_run = l_run * alpha + wave_sum(p);
+    m_run = m_new;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+
+#pragma unroll
+    for (int vb = 0; vb < NV; vb += VB) {
+      if (vb > 0) {  // only for fp32 with wide V rows: next batch of loads
+#pragma unroll
+        for (int u = 0; u < VB; ++u) {
+          const int r = t0 + (vb + u) * RPL_V + vr;
+          vv[u] = r < rows ? load16(vp + (size_t)r * DV) : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < VB; ++u) {
+        const int r = (vb + u) * RPL_V + vr;  // row within the tile
+        const float pr = __shfl(p, (r % RPL_K) * LPR_K + r / RPL_K);
+        float vf[EPL];
+        Elem<T>::unpack(vv[u], vf);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pr, vf[e], acc[e]);
+      }
+    }
+  }
+
+  // Sum the row groups of the wave (lanes with equal vl).
+#pragma unroll
+  for (int off = LPR_V; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], off);
+  }
+  const size_t pidx = ((size_t)b * n_q + i) * C + c;
+  if (vr == 0) {
+    f32x4* dst = reinterpret_cast<f32x4*>(part_acc + pidx * DV + vl * EPL);
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) dst[e / 4] = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+  }
+  if (lane == 0) {
+    part_ml[2 * pidx] = m_run;
+    part_ml[2 * pidx + 1] = l_run;
+  }
+}
+
+constexpr int kCombineThreads = 256;
+
+template <typename T, int DV>
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
+    const float* __restrict__ part_ml, const float* __restrict__ part_acc,
+    const int32_t* __restrict__ ctx_len, T* __restrict__ out,
+    float* __restrict__ lse, int n_q, int l_cap, int max_ctx, int S, int C) {
+  constexpr int LPR = DV / 4;                 // lanes per partial row (float4)
+  constexpr int CPP = kCombineThreads / LPR;  // partials per pass
+  static_assert(LPR <= kCombineThreads, "d_v");
+  extern __shared__ float smem[];
+  float* w_s = smem;                      // [C] chunk weights
+  float* red_s = smem + ((C + 3) & ~3);   // [CPP][DV] partial sums (16-byte aligned)
+  __shared__ float wred[kCombineThreads / 64];
+
+  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int L = ctx_len[b];
+  L = max(0, min(L, min(max_ctx, l_cap)));
+  const int nc = min(C, (L + S - 1) / S);
+  const size_t base = ((size_t)b * n_q + i) * C;
+
+  float M = -INFINITY;
+  for (int c = tid; c < nc; c += kCombineThreads) M = fmaxf(M, part_ml[2 * (base + c)]);
+  M = wave_max(M);
+  if (lane == 0) wred[wave] = M;
+  __syncthreads();
+  M = wred[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, wred[w]);
+  __syncthreads();
+
+  float lam = 0.f;
+  for (int c = tid; c < nc; c += kCombineThreads) {
+    const float w = fast_exp2(part_ml[2 * (base + c)] - M);
+    w_s[c] = w;
+    lam += w * part_ml[2 * (base + c) + 1];
+  }
+  lam = wave_sum(lam);
+  if (lane == 0) wred[wave] = lam;
+  __syncthreads();
+  lam = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCombineThreads / 64; ++w) lam += wred[w];
+
+  const int cl = tid % LPR, cr = tid / LPR;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  const float* src = part_acc + base * DV + cl * 4;
+  int c = cr;
+  for (; c + 3 * CPP < nc; c += 4 * CPP) {
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(src + (size_t)c * DV);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + (size_t)(c + CPP) * DV);
+    const f32x4 a2 = *reinterpret_cast<const f32x4*>(src + (size_t)(c + 2 * CPP) * DV);
+    const f32x4 a3 = *reinterpret_cast<const f32x4*>(src + (size_t)(c + 3 * CPP) * DV);
+    o += w_s[c] * a0;
+    o += w_s[c + CPP] * a1;
+    o += w_s[c + 2 * CPP] * a2;
+    o += w_s[c + 3 * CPP] * a3;
+  }
+  for (; c < nc; c += CPP) o += w_s[c] * *reinterpret_cast<const f32x4*>(src + (size_t)c * DV);
+
+  if (CPP > 1) {
+    *reinterpret_cast<f32x4*>(red_s + cr * DV + cl * 4) = o;
+    __syncthreads();
+    if (cr == 0) {
+      for (int k = 1; k < CPP; ++k) o += *reinterpret_cast<const f32x4*>(red_s + k * DV + cl * 4);
+    }
+  }
+  if (cr == 0) {
+    const float inv = nc > 0 ? 1.f / lam : 0.f;
+    T* dst = out + ((size_t)b * n_q + i) * DV + cl * 4;
+    dst[0] = Elem<T>::from_f32(o.x * inv);
+    dst[1] = Elem<T>::from_f32(o.y * inv);
+    dst[2] = Elem<T>::from_f32(o.z * inv);
+    dst[3] = Elem<T>::from_f32(o.w * inv);
+  }
+  if (tid == 0 && lse != nullptr)
+    lse[(size_t)b * n_q + i] = nc > 0 ? (M + fast_log2(lam)) * kLn2 : -INFINITY;
+}
+
+// ------------------------------------------------------------------ launch
+
+template <typename T, int DK, int DV>
+static hipError_t launch_split_t(const DecodeArgs& a) {
+  const float qscale = a.scale * kLog2e;
+  dim3 grid(a.C, (a.n_q + 3) / 4, a.batch);
+  hipLaunchKernelGGL((decode_split_kernel<T, DK, DV>), grid, dim3(256), 0, a.stream,
+                     (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.ctx_len,
+                     a.part_ml, a.part_acc, a.n_q, a.n_k, a.n_v, a.l_cap, a.max_ctx, a.S,
+                     a.C, qscale);
+  return hipGetLastError();
+}
+
+template <typename T, int DV>
+static hipError_t launch_combine_t(const DecodeArgs& a) {
+  constexpr int CPP = kCombineThreads / (DV / 4);
+  const size_t lds = ((size_t)((a.C + 3) & ~3) + (size_t)CPP * DV) * sizeof(float);
+  dim3 grid(a.n_q, a.batch);
+  hipLaunchKernelGGL((decode_combine_kernel<T, DV>), grid, dim3(kCombineThreads), lds,
+                     a.stream, a.part_ml, a.part_acc, a.ctx_len, (T*)a.out, a.lse, a.n_q,
+                     a.l_cap, a.max_ctx, a.S, a.C);
+  return hipGetLastError();
+}
+
+template <typename T, int DK>
+static hipError_t split_dv(const DecodeArgs& a) {
+  switch (a.d_v) {
+    case 32: return launch_split_t<T, DK, 32>(a);
+    case 64: return launch_split_t<T, DK, 64>(a);
+    case 128: return launch_split_t<T, DK, 128>(a);
+    case 256: return launch_split_t<T, DK, 256>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t split_dk(const DecodeArgs& a) {
+  switch (a.d_k) {
+    case 32: return split_dv<T, 32>(a);
+    case 64: return split_dv<T, 64>(a);
+    case 128: return split_dv<T, 128>(a);
+    case 256:
+      if constexpr (sizeof(T) == 2) return split_dv<T, 256>(a);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t combine_dv(const DecodeArgs& a) {
+  switch (a.d_v) {
+    case 32: return launch_combine_t<T, 32>(a);
+    case 64: return launch_combine_t<T, 64>(a);
+    case 128: return launch_combine_t<T, 128>(a);
+    case 256: return launch_combine_t<T, 256>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_split(const DecodeArgs& a) {
+  return a.bf16 ? split_dk<bf16>(a) : split_dk<float>(a);
+}
+
+hipError_t launch_decode_combine(const DecodeArgs& a) {
+  return a.bf16 ? combine_dv<bf16>(a) : combine_dv<float>(a);
+}
+
+}  // namespace dqkv

@@ -1,0 +1,58 @@
+// Host-side launch descriptors shared by the C ABI (api.hip) and the kernel
+// translation units.  Sizes are validated by the ABI layer before a launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dqkv {
+
+struct DecodeArgs {
+  bool bf16;
+  int n_q, n_k, n_v, d_k, d_v;
+  int batch, l_cap, max_ctx;
+  int S, C;  // chunk rows, chunks per sequence
+  float scale;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* ctx_len;
+  void* out;
+  float* lse;
+  float* part_ml;   // [B][n_q][C][2]
+  float* part_acc;  // [B][n_q][C][d_v]
+  hipStream_t stream;
+};
+
+struct AppendArgs {
+  int elem_bytes;
+  int n_k, n_v, d_k, d_v;
+  int batch, t_new, l_cap;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* pos;
+  void* k_cache;
+  void* v_cache;
+  hipStream_t stream;
+};
+
+struct PrefillArgs {
+  int n_q, n_k, n_v, d_k, d_v;
+  int batch, t_new, l_cap;
+  float scale;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* ctx_len;
+  void* out;
+  float* lse;
+  hipStream_t stream;
+};
+
+hipError_t launch_decode_split(const DecodeArgs& a);
+hipError_t launch_decode_combine(const DecodeArgs& a);
+hipError_t launch_kv_append(const AppendArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a);
+
+}  // namespace dqkv

@@ -1,0 +1,391 @@
+#!/usr/bin/env python3
+"""Benchmark of the DiffQKV decode hot path on one MI355X.
+
+One step = one decode step of the workload: kv_append of the newest K/V row
+of every sequence, then the split-KV decode kernel, then the combine kernel
+(the path's store, split and combine steps).  Inputs are seeded synthetic
+caches, resident in HBM before timing starts.  Each step attends a different
+replica of the caches (standing for successive layers) so that the replicas
+together exceed the 256 MB Infinity Cache several times over and the timing
+reflects HBM, not the last-level cache.
+
+The timed steps are captured once in a HIP graph and replayed (the launch
+rate of three small kernels from Python would otherwise bound the step);
+a second, eager pass brackets every kernel with events on the launch stream
+for the per-kernel durations the roofline uses.
+
+Prints one JSON line.  ``value`` is the algorithmic HBM bytes of a step
+(sum over sequences of ctx_len * (n_k d_k + n_v d_v) * element size, plus q,
+out and the appended rows) divided by the measured step time.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode µs/step & achieved HBM GB/s (% of peak) at 32k/64k ctx, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode32k_asym")
+    p.add_argument("--twin", default=None,
+                   help="symmetric workload timed for the speedup (default: by workload)")
+    p.add_argument("--no-twin", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--chunk", type=int, default=0, help="decode chunk rows (0 = auto)")
+    p.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    p.add_argument("--kernel-only", action="store_true",
+                   help="only run steps (for profilers); skip twin, prefill, CPU baseline")
+    return p.parse_args()
+
+
+TWINS = {"decode32k_asym": "decode32k_sym", "decode64k_dk64": "decode64k_sym",
+         "decode64k_dk128": "decode64k_sym"}
+
+
+# ----------------------------------------------------------------- device side
+
+class DecodeBench:
+    """Device buffers and raw C-ABI argument tuples for one decode workload."""
+
+    def __init__(self, name: str, chunk: int = 0):
+        import numpy as np
+        import torch
+
+        import asymmetric_head_kv_amd as dq
+        import synth
+
+        self.torch, self.dq = torch, dq
+        self.lib = dq.load()
+        self.name = name
+        wl = synth.workload(name)
+        append_lens = name == "ragged16"
+        case = synth.make_case(**wl)
+        self.case = case
+        B, n_q, n_k, n_v, d_k, d_v = (case.batch, case.n_q, case.n_k, case.n_v,
+                                      case.d_k, case.d_v)
+        self.shape = (n_q, n_k, n_v, d_k, d_v)
+        self.B, self.l_cap = B, case.l_cap
+        esize = 2 if case.dtype == "bf16" else 4
+        self.esize = esize
+        self.dtype_code = dq.BF16 if case.dtype == "bf16" else dq.F32
+        if append_lens:   # cache holds ctx_len rows; append one, attend ctx_len + 1
+            pos = np.asarray(case.ctx_len, dtype=np.int64)
+            ctx = pos + 1
+        else:             # the newest of ctx_len rows is (re)written by the append
+            ctx = np.asarray(case.ctx_len, dtype=np.int64)
+            pos = ctx - 1
+        self.ctx = ctx
+        self.max_ctx = int(ctx.max())
+        k_new, v_new = synth.new_rows(wl["seed"], dtype=case.dtype, batch=B, t_new=1, n_k=n_k,
+                                      n_v=n_v, d_k=d_k, d_v=d_v)
+        dev = "cuda"
+
+        def up(a):
+            if case.dtype == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                    torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        self.q = up(case.q)
+        k0, v0 = up(case.k_cache), up(case.v_cache)
+        self.k_new, self.v_new = up(k_new), up(v_new)
+        self.pos = torch.from_numpy(pos.astype(np.int32)).to(dev)
+        self.ctx_t = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+        beta = (n_k * d_k + n_v * d_v) * esize
+        self.cache_bytes_attended = int(ctx.sum()) * beta
+        self.alg_bytes_split = self.cache_bytes_attended + B * n_q * d_k * esize
+        self.alg_bytes_step = (self.alg_bytes_split + B * n_q * d_v * esize
+                               + B * beta)  # + out + appended rows
+        footprint = (k0.numel() + v0.numel()) * esize
+        self.replicas = max(2, min(16, math.ceil(4 * MALL_BYTES / max(1, footprint))))
+        self.caches = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(self.replicas - 1)]
+        self.out = torch.empty((B, n_q, d_v), dtype=self.q.dtype, device=dev)
+        self.lse = torch.empty((B, n_q), dtype=torch.float32, device=dev)
+        self.chunk = chunk
+        self.ws_bytes = dq.decode_workspace_bytes(*self.shape, B, self.max_ctx, chunk)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.S = chunk or dq.decode_chunk(*self.shape, B, self.max_ctx)
+        self.flops = 2 * n_q * (d_k + d_v) * int(ctx.sum())
+
+    def _stream(self):
+        return self.torch.cuda.current_stream().cuda_stream
+
+    def append(self, r):
+        k, v = self.caches[r]
+        st = self.lib.kv_append(*self.shape, self.dtype_code, self.B, 1, self.l_cap,
+                                self.k_new.data_ptr(), self.v_new.data_ptr(),
+                                self.pos.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                self._stream())
+        assert st == 0, st
+
+    def split(self, r):
+        k, v = self.caches[r]
+        st = self.lib.diffqkv_decode_split(
+            *self.shape, self.dtype_code, self.B, self.l_cap, self.max_ctx, self.case.scale,
+            self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.ctx_t.data_ptr(), self.chunk,
+            self.ws.data_ptr(), self.ws_bytes, self._stream())
+        assert st == 0, st
+
+    def combine(self):
+        st = self.lib.diffqkv_decode_combine(
+            *self.shape, self.dtype_code, self.B, self.l_cap, self.max_ctx,
+            self.ctx_t.data_ptr(), self.out.data_ptr(), self.lse.data_ptr(), self.chunk,
+            self.ws.data_ptr(), self.ws_bytes, self._stream())
+        assert st == 0, st
+
+    def step(self, r):
+        self.append(r)
+        self.split(r)
+        self.combine()
+
+    # -- timing -------------------------------------------------------------
+
+    def time_steps(self, steps: int, warmup: int, eager: bool = False):
+        """Average ms per step over exactly `steps` steps (graph replay)."""
+        torch = self.torch
+        R = self.replicas
+        for w in range(warmup):
+            self.step(w % R)
+        torch.cuda.synchronize()
+        graphs = {}
+        if not eager:
+            try:
+                for n in {R, steps % R} - {0}:
+                    g = torch.cuda.CUDAGraph()
+                    s = torch.cuda.Stream()
+                    s.wait_stream(torch.cuda.current_stream())
+                    with torch.cuda.stream(s):
+                        self.step(0)
+                    torch.cuda.current_stream().wait_stream(s)
+                    with torch.cuda.graph(g):
+                        for r in range(n):
+                            self.step(r)
+                    graphs[n] = g
+                for g in graphs.values():  # warm replays
+                    g.replay()
+                torch.cuda.synchronize()
+            except Exception as e:  # fall back to eager timing
+                log(f"graph capture failed ({e}); timing eager launches")
+                graphs = {}
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        if graphs:
+            for _ in range(steps // R):
+                graphs[R].replay()
+            if steps % R:
+                graphs[steps % R].replay()
+        else:
+            for s in range(steps):
+                self.step(s % R)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps, bool(graphs)
+
+    def time_kernels(self, steps: int):
+        """Per-kernel average durations (ms) from events on the launch stream."""
+        torch = self.torch
+        R = self.replicas
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for s in range(steps):
+            e = ev[s]
+            e[0].record()
+            self.append(s % R)
+            e[1].record()
+            self.split(s % R)
+            e[2].record()
+            self.combine()
+            e[3].record()
+        torch.cuda.synchronize()
+        tot = [0.0, 0.0, 0.0]
+        for e in ev:
+            for k in range(3):
+                tot[k] += e[k].elapsed_time(e[k + 1])
+        return [t / steps for t in tot]
+
+    def free(self):
+        self.caches = None
+        self.torch.cuda.empty_cache()
+
+
+def prefill_bench(steps: int = 10):
+    import numpy as np
+    import torch
+
+    import asymmetric_head_kv_amd as dq
+    import synth
+
+    case = synth.make_case(**synth.workload("prefill2k_on_30k"))
+    dev = "cuda"
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(case.q), up(case.k_cache), up(case.v_cache)
+    ctx = torch.from_numpy(case.ctx_len.astype(np.int32)).to(dev)
+    out = torch.empty((case.batch, case.t_new, case.n_q, case.d_v), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        dq.prefill(q, k, v, ctx, out=out)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        dq.prefill(q, k, v, ctx, out=out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    L, T = int(case.ctx_len[0]), case.t_new
+    pairs = sum(L - T + r + 1 for r in range(T))
+    flops = pairs * case.n_q * 2 * (case.d_k + case.d_v)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": "prefill2k_on_30k", "us_per_call": round(ms * 1e3, 2),
+            "algorithmic_gflop": round(flops / 1e9, 2), "tflops": round(tflops, 1),
+            "bound": "mfma", "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+
+
+def hbm_copy_gbs(nbytes: int = 2 << 30, reps: int = 10):
+    """Practical HBM ceiling: a large device-to-device copy (read + write)."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(name: str, seconds: float):
+    """The fp64 oracle on the same workload, timed on the host cores."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
+    except Exception:
+        threads = 1
+    case = synth.make_case(**synth.workload(name))
+    q, k, v = case.widened()
+    ctx = np.asarray(case.ctx_len)
+    esize = 2 if case.dtype == "bf16" else 4
+    byts = int(ctx.sum()) * (case.n_k * case.d_k + case.n_v * case.d_v) * esize
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.decode(q, k, v, ctx, case.scale)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / n
+    return {"value": round(byts / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "us_per_step": round(per * 1e6, 1),
+            "sample": f"{n} full decode steps of {name} (fp64 numpy oracle, "
+                      f"{threads} BLAS threads, {el:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
+              "is not sharded across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    log(f"workload {args.workload}: building inputs")
+    bench = DecodeBench(args.workload, args.chunk)
+    log(f"replicas {bench.replicas}, chunk {bench.S} rows, workspace {bench.ws_bytes} B")
+    ms, graphed = bench.time_steps(args.steps, args.warmup, args.eager)
+    log(f"step {ms * 1e3:.2f} us ({'graph' if graphed else 'eager'})")
+    k_ms = bench.time_kernels(args.steps)
+    log("kernels (us): append %.2f split %.2f combine %.2f" % tuple(x * 1e3 for x in k_ms))
+    split_gbs = bench.alg_bytes_split / (k_ms[1] * 1e-3) / 1e9
+    value = bench.alg_bytes_step / (ms * 1e-3) / 1e9
+    n_q, n_k, n_v, d_k, d_v = bench.shape
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": bench.case.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "batch": bench.B, "max_ctx": bench.max_ctx,
+                   "n_q": n_q, "n_k": n_k, "n_v": n_v, "d_k": d_k, "d_v": d_v,
+                   "chunk_rows": bench.S, "cache_replicas": bench.replicas,
+                   "timing": "hip graph replay" if graphed else "eager launches",
+                   "step": "kv_append(1 row/seq) + split + combine"},
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel",
+                     "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": bench.alg_bytes_split,
+                     "avg_launch_us": round(k_ms[1] * 1e3, 2)},
+        "kernels_us": {"kv_append": round(k_ms[0] * 1e3, 2), "split": round(k_ms[1] * 1e3, 2),
+                       "combine": round(k_ms[2] * 1e3, 2)},
+    }
+    sym_name = None if args.no_twin else (args.twin or TWINS.get(args.workload))
+    asym_bytes = bench.alg_bytes_step
+    bench.free()
+    del bench
+    if not args.kernel_only:
+        if sym_name:
+            log(f"symmetric twin {sym_name}")
+            tw = DecodeBench(sym_name, args.chunk)
+            ms_t, _ = tw.time_steps(args.steps, args.warmup, args.eager)
+            result["symmetric_twin"] = {
+                "workload": sym_name, "us_per_step": round(ms_t * 1e3, 2),
+                "GBps": round(tw.alg_bytes_step / (ms_t * 1e-3) / 1e9, 1),
+                "speedup_asym_over_sym": round(ms_t / ms, 3),
+                "byte_ratio_bound": round(tw.alg_bytes_step / asym_bytes, 3)}
+            tw.free()
+            del tw
+        try:
+            result["hbm_copy_GBps"] = round(hbm_copy_gbs(), 1)
+        except Exception as e:
+            log(f"copy bandwidth probe failed: {e}")
+        if not args.no_prefill:
+            log("prefill 2048 on 30720")
+            result["prefill"] = prefill_bench()
+        if not args.no_cpu_baseline:
+            log("cpu baseline (oracle)")
+            result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * diffqkv.h -- C ABI of the DiffQKV attention library for AMD MI355X (gfx950).
+ *
+ * DiffQKV attention (the Sigma pages: "Sigma: Differential Rescaling of
+ * Query, Key and Value for Efficient Language Models", architecture summary
+ * page, sections 3.2 and 3.4, and its "FlexHeadFA Kernel and Deployment
+ * Infrastructure" section) lets the Query, Key and Value sides carry their
+ * own head counts and head dimensions:
+ *
+ *   n_q query heads of dimension d_k (the query is already in the key space),
+ *   n_k key heads of dimension d_k, n_v value heads of dimension d_v.
+ *
+ * Query head i reads key head floor(i * n_k / n_q) and value head
+ * floor(i * n_v / n_q) (section 3.4 Step 3, GroupSharing; FlexHeadFA's
+ * separated address rule).  Its output is
+ *
+ *   o_i = sum_j softmax_j(scale * q_i . K_j) * V_j,   o_i in R^{d_v}
+ *
+ * (section 3.4 Steps 4 and 5), scale = 1/sqrt(d_k) unless the caller passes
+ * another positive value.
+ *
+ * Memory layouts (row-major, innermost last; all device memory):
+ *   q (decode)   [B][n_q][d_k]
+ *   q (prefill)  [B][t_new][n_q][d_k]
+ *   k_cache      [B][n_k][l_cap][d_k]    separate key cache  (section 3.2 item 3)
+ *   v_cache      [B][n_v][l_cap][d_v]    separate value cache
+ *   k_new        [B][t_new][n_k][d_k]    token-major rows to append
+ *   v_new        [B][t_new][n_v][d_v]
+ *   out (decode) [B][n_q][d_v],  lse (decode)  [B][n_q]         (fp32)
+ *   out (prefill)[B][t_new][n_q][d_v], lse      [B][t_new][n_q] (fp32)
+ *   ctx_len, pos [B] int32
+ *
+ * Element type: DQKV_F32 (IEEE float) or DQKV_BF16 (bfloat16 bit patterns) for
+ * q, caches, new rows and out; arithmetic is fp32 throughout, bf16 outputs are
+ * rounded to nearest even.  lse is the natural-log log-sum-exp of the scaled
+ * scores, always fp32, optional (NULL to skip).
+ *
+ * Supported sizes: 1 <= n_k <= n_q, 1 <= n_v <= n_q, n_q a multiple of n_k
+ * and of n_v, n_q / n_k <= 16; d_k, d_v in {32, 64, 128, 256} (prefill: d_k
+ * in {64, 128}, d_v in {64, 128}, bf16 only).  Every device pointer must be
+ * 16-byte aligned.
+ *
+ * Ownership and execution: the caller owns every buffer; the library neither
+ * allocates nor frees device memory nor keeps any pointer after returning.
+ * Every call only enqueues work on `stream` (a hipStream_t; NULL = the null
+ * stream) and never synchronises.  The return value reports host-side
+ * argument checks and launch errors (DQKV_ERR_HIP); faults inside a kernel
+ * surface at the caller's next synchronisation.  Calls on one stream run in
+ * order; calls that share output buffers on different streams race.
+ */
+#ifndef DIFFQKV_H
+#define DIFFQKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+#define DQKV_F32  0
+#define DQKV_BF16 1
+
+/* Status codes. */
+#define DQKV_OK               0
+#define DQKV_ERR_NULL        -1 /* a required pointer is NULL                 */
+#define DQKV_ERR_SHAPE       -2 /* head counts / sizes violate the rules above */
+#define DQKV_ERR_UNSUPPORTED -3 /* valid, but a size or dtype not built        */
+#define DQKV_ERR_WORKSPACE   -4 /* workspace too small                         */
+#define DQKV_ERR_HIP         -5 /* the HIP runtime refused a launch            */
+#define DQKV_ERR_ALIGN       -6 /* a device pointer is not 16-byte aligned     */
+
+/* Human-readable name of a status code (static storage). */
+const char* dqkv_status_str(int32_t status);
+
+/*
+ * Context-chunk length (rows per split) that diffqkv_decode uses when it is
+ * called with chunk_tokens = 0.  Pure host computation.
+ */
+int32_t diffqkv_decode_chunk(int32_t n_q, int32_t n_k, int32_t n_v,
+                             int32_t d_k, int32_t d_v, int32_t batch,
+                             int32_t max_ctx, int32_t* chunk_tokens);
+
+/*
+ * Workspace bytes diffqkv_decode needs for these sizes and chunk length
+ * (chunk_tokens = 0: the automatic choice).  The workspace holds the
+ * per-chunk partial results (running max, sum and weighted V sum, fp32) of
+ * the split step.  Pure host computation.
+ */
+int32_t diffqkv_decode_workspace(int32_t n_q, int32_t n_k, int32_t n_v,
+                                 int32_t d_k, int32_t d_v, int32_t batch,
+                                 int32_t max_ctx, int32_t chunk_tokens,
+                                 size_t* bytes);
+
+/*
+ * kv_append -- Step 2 of section 3.4: K_t = [K_{t-1}; k_t], V_t = [V_{t-1}; v_t]
+ * into the separate K and V caches.
+ *
+ * Token t of sequence b (k_new[b][t], v_new[b][t]) is copied, bit for bit,
+ * to cache row pos[b] + t of every head.  pos is a device array.  Rows whose
+ * destination falls outside [0, l_cap) are skipped (no write).  t_new = 0 or
+ * batch = 0 is a no-op.
+ */
+int32_t kv_append(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                  int32_t d_v, int32_t dtype, int32_t batch, int32_t t_new,
+                  int32_t l_cap, const void* k_new, const void* v_new,
+                  const int32_t* pos, void* k_cache, void* v_cache,
+                  void* stream);
+
+/*
+ * diffqkv_decode -- one decode step: every query head of every sequence
+ * attends rows 0 .. ctx_len[b]-1 of its key and value heads (the newest row
+ * included, section 3.4 Steps 2-5).
+ *
+ * Split-KV structure (FlexHeadFA section: a split kernel over context chunks
+ * followed by a combine kernel): the context is cut into chunks of
+ * chunk_tokens rows (0 = automatic, otherwise a multiple of 64); the split
+ * kernel writes each chunk's (max, sum, weighted V sum) into `workspace`
+ * (>= diffqkv_decode_workspace bytes, 16-byte aligned, contents need not be
+ * initialised) and the combine kernel merges them exactly in log-sum-exp
+ * form into out and lse.
+ *
+ * max_ctx (host) bounds ctx_len and sizes the launch: 0 <= ctx_len[b] <=
+ * max_ctx <= l_cap is required.  Values beyond are clamped to
+ * min(max_ctx, l_cap) (memory-safe, result then covers only those rows).
+ * ctx_len[b] = 0 yields out = 0 and lse = -inf.
+ */
+int32_t diffqkv_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                       int32_t d_v, int32_t dtype, int32_t batch,
+                       int32_t l_cap, int32_t max_ctx, float scale,
+                       const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* ctx_len,
+                       void* out, float* lse, int32_t chunk_tokens,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * diffqkv_decode_split / diffqkv_decode_combine -- the two halves of
+ * diffqkv_decode, for callers that time or schedule them separately (the
+ * pages measure the split and combine kernels of FlexHeadFA separately).
+ * Arguments have the meaning given for diffqkv_decode; both calls of one
+ * step must pass the same sizes, chunk_tokens and workspace.  The split
+ * kernel writes every non-empty chunk's (max, sum, weighted V sum) to the
+ * workspace; the combine reads them and writes out and lse.
+ */
+int32_t diffqkv_decode_split(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                             int32_t d_v, int32_t dtype, int32_t batch,
+                             int32_t l_cap, int32_t max_ctx, float scale,
+                             const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* ctx_len,
+                             int32_t chunk_tokens, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+int32_t diffqkv_decode_combine(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                               int32_t d_v, int32_t dtype, int32_t batch,
+                               int32_t l_cap, int32_t max_ctx,
+                               const int32_t* ctx_len, void* out, float* lse,
+                               int32_t chunk_tokens, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * diffqkv_prefill -- causal attention of t_new new query rows per sequence
+ * against the cache, with bf16 matrix-core (MFMA) products.
+ *
+ * The t_new new rows must already be in the caches (kv_append), so
+ * ctx_len[b] counts rows after the append and ctx_len[b] >= t_new.  New row
+ * r of sequence b sits at position p = ctx_len[b] - t_new + r and attends
+ * key rows 0 .. p (each token sees all earlier tokens and itself; a reading
+ * of section 3.4 Steps 2-5 applied token by token).  Rows with p < 0 (that
+ * is ctx_len[b] < t_new) get out = 0, lse = -inf; ctx_len is clamped to
+ * l_cap.
+ */
+int32_t diffqkv_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                        int32_t d_v, int32_t dtype, int32_t batch,
+                        int32_t t_new, int32_t l_cap, float scale,
+                        const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* ctx_len,
+                        void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFQKV_H */

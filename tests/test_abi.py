@@ -1,0 +1,157 @@
+"""The C ABI on the CPU: the library loads, exports what include/diffqkv.h
+declares, and its host-side checks reject bad arguments before any launch.
+
+Every call here fails validation (or is a pure host query), so no HIP call is
+made; fake device pointers are 16-byte-aligned integers never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "diffqkv.h")
+
+dq = pytest.importorskip("asymmetric_head_kv_amd")
+
+OK, NULL, SHAPE, UNSUP, WS, HIP, ALIGN = 0, -1, -2, -3, -4, -5, -6
+FAKE = 1 << 20  # aligned, never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dq.lib_path):
+        pytest.skip("libdiffqkv.so not built")
+    return dq.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    assert {"diffqkv_decode", "diffqkv_prefill", "kv_append", "diffqkv_decode_workspace",
+            "diffqkv_decode_chunk", "dqkv_status_str"} <= names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(dq.SIGNATURES) == _declared()
+
+
+def test_status_strings(lib):
+    for code, name in dq.STATUS.items():
+        assert lib.dqkv_status_str(code).decode().startswith(name)
+    assert b"unknown" in lib.dqkv_status_str(42)
+
+
+def _decode(lib, n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=1, l_cap=1024,
+            max_ctx=1024, scale=0.125, q=FAKE, k=FAKE, v=FAKE, ctx=FAKE, out=FAKE,
+            lse=None, chunk=0, ws=FAKE, ws_bytes=0):
+    return lib.diffqkv_decode(n_q, n_k, n_v, d_k, d_v, dtype, B, l_cap, max_ctx, scale,
+                              q, k, v, ctx, out, lse, chunk, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("heads,code", [
+    ((16, 3, 16), SHAPE),   # n_q not a multiple of n_k
+    ((16, 4, 6), SHAPE),    # n_q not a multiple of n_v
+    ((16, 32, 16), SHAPE),  # more K heads than query heads
+    ((16, 4, 32), SHAPE),   # more V heads than query heads
+    ((0, 1, 1), SHAPE),
+    ((16, 0, 16), SHAPE),
+])
+def test_decode_rejects_bad_head_counts(lib, heads, code):
+    n_q, n_k, n_v = heads
+    assert _decode(lib, n_q=n_q, n_k=n_k, n_v=n_v) == code
+
+
+def test_decode_rejects_unsupported_and_bad_sizes(lib):
+    assert _decode(lib, d_k=48) == UNSUP
+    assert _decode(lib, d_v=96) == UNSUP
+    assert _decode(lib, dtype=7) == UNSUP
+    assert _decode(lib, dtype=0, d_k=256) == UNSUP
+    assert _decode(lib, max_ctx=2048, l_cap=1024) == SHAPE
+    assert _decode(lib, B=-1) == SHAPE
+    assert _decode(lib, scale=0.0) == SHAPE
+    assert _decode(lib, scale=float("nan")) == SHAPE
+    assert _decode(lib, chunk=100) == SHAPE   # not a multiple of 64
+    assert _decode(lib, chunk=-64) == SHAPE
+
+
+def test_decode_null_alignment_and_workspace(lib):
+    assert _decode(lib, q=None) == NULL
+    assert _decode(lib, ctx=None) == NULL
+    assert _decode(lib, ws=None) == NULL
+    assert _decode(lib, k=FAKE + 8) == ALIGN
+    assert _decode(lib, out=FAKE + 2) == ALIGN
+    need = dq.decode_workspace_bytes(16, 4, 16, 64, 128, 1, 1024)
+    assert _decode(lib, ws_bytes=need - 1) == WS
+    assert _decode(lib, B=0) == OK  # nothing to do, nothing launched
+
+
+def test_workspace_and_chunk_plan(lib):
+    # Partials: (m, l) then acc[d_v], fp32, per (sequence, query head, chunk).
+    for (B, n_q, d_v, ctx) in [(1, 16, 128, 32768), (16, 16, 128, 32769), (4, 16, 128, 65536),
+                               (1, 4, 64, 256)]:
+        S = dq.decode_chunk(n_q, 4 if n_q > 4 else 1, n_q, 64, d_v, B, ctx)
+        assert S % 64 == 0 and S >= 64
+        C = -(-ctx // S)
+        parts = B * n_q * C
+        expect = -(-parts * 8 // 256) * 256 + parts * d_v * 4
+        assert dq.decode_workspace_bytes(n_q, 4 if n_q > 4 else 1, n_q, 64, d_v, B, ctx) == expect
+    # Long single sequence: enough chunks to spread over the chip.
+    S = dq.decode_chunk(16, 4, 16, 64, 128, 1, 32768)
+    assert 32768 // S >= 64
+    # Explicit chunk lengths are honoured.
+    assert dq.decode_workspace_bytes(16, 4, 16, 64, 128, 1, 4096, 64) == \
+        -(-16 * 64 * 8 // 256) * 256 + 16 * 64 * 128 * 4
+    with pytest.raises(dq.DQKVError):
+        dq.decode_workspace_bytes(16, 4, 16, 64, 128, 1, 1 << 30, 64)  # too many chunks
+
+
+def test_kv_append_validation(lib):
+    def call(**kw):
+        a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=2, T=1, l_cap=100,
+                 kn=FAKE, vn=FAKE, pos=FAKE, kc=FAKE, vc=FAKE)
+        a.update(kw)
+        return lib.kv_append(a["n_q"], a["n_k"], a["n_v"], a["d_k"], a["d_v"], a["dtype"],
+                             a["B"], a["T"], a["l_cap"], a["kn"], a["vn"], a["pos"], a["kc"],
+                             a["vc"], None)
+    assert call(n_k=5) == SHAPE
+    assert call(d_v=100) == UNSUP
+    assert call(pos=None) == NULL
+    assert call(vc=FAKE + 4) == ALIGN
+    assert call(T=0) == OK and call(B=0) == OK
+    assert call(T=-1) == SHAPE
+
+
+def test_prefill_validation(lib):
+    def call(**kw):
+        a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=1, T=128, l_cap=1024,
+                 scale=0.125, q=FAKE, kc=FAKE, vc=FAKE, ctx=FAKE, out=FAKE, lse=None)
+        a.update(kw)
+        return lib.diffqkv_prefill(a["n_q"], a["n_k"], a["n_v"], a["d_k"], a["d_v"], a["dtype"],
+                                   a["B"], a["T"], a["l_cap"], a["scale"], a["q"], a["kc"],
+                                   a["vc"], a["ctx"], a["out"], a["lse"], None)
+    assert call(dtype=0) == UNSUP
+    assert call(d_k=32) == UNSUP
+    assert call(d_v=256) == UNSUP
+    assert call(n_v=5) == SHAPE
+    assert call(out=None) == NULL
+    assert call(q=FAKE + 2) == ALIGN
+    assert call(T=0) == OK
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 4, 32)
+    k = torch.zeros(1, 1, 8, 32)
+    v = torch.zeros(1, 4, 8, 64)
+    with pytest.raises(ValueError):
+        dq.decode(q, k, v, torch.zeros(1, dtype=torch.int32))

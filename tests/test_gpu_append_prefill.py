@@ -1,0 +1,149 @@
+"""GPU parity of kv_append (bit-exact) and of the MFMA causal prefill."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_close, assert_lse_close, ints_to_dev, raw_host, to_dev, to_host, upload
+
+pytestmark = pytest.mark.gpu
+dq = pytest.importorskip("asymmetric_head_kv_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dq.load()
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _bits(shape, seed):
+    return np.random.default_rng(seed).integers(0, 65536, shape, dtype=np.uint16)
+
+
+# ----------------------------------------------------------------- kv_append
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kv_append_bit_exact(dtype):
+    B, T, n_k, n_v, d_k, d_v, cap = 3, 5, 4, 16, 64, 128, 100
+    if dtype == "bf16":
+        kc, vc = _bits((B, n_k, cap, d_k), 1), _bits((B, n_v, cap, d_v), 2)
+        kn, vn = _bits((B, T, n_k, d_k), 3), _bits((B, T, n_v, d_v), 4)
+    else:  # arbitrary 32-bit patterns, NaNs included, must survive unchanged
+        rng = np.random.default_rng(5)
+        kc, vc = (rng.integers(0, 2**32, s, dtype=np.uint32).view(np.float32)
+                  for s in ((B, n_k, cap, d_k), (B, n_v, cap, d_v)))
+        kn, vn = (rng.integers(0, 2**32, s, dtype=np.uint32).view(np.float32)
+                  for s in ((B, T, n_k, d_k), (B, T, n_v, d_v)))
+    pos = np.array([0, 40, cap - T])
+    _say("kv_append", dtype)
+    k, v = to_dev(kc, dtype), to_dev(vc, dtype)
+    dq.kv_append(to_dev(kn, dtype), to_dev(vn, dtype), ints_to_dev(pos), k, v, n_q=16)
+    torch.cuda.synchronize()
+    ek, ev = oracle.kv_append(kc, vc, kn, vn, pos)
+    gk, gv = raw_host(k), raw_host(v)
+    np.testing.assert_array_equal(gk.view(np.uint8), np.asarray(ek).view(np.uint8))
+    np.testing.assert_array_equal(gv.view(np.uint8), np.asarray(ev).view(np.uint8))
+
+
+def test_kv_append_skips_rows_outside_cache():
+    B, T, n_k, n_v, d_k, d_v, cap = 2, 4, 1, 2, 32, 64, 10
+    kc, vc = _bits((B, n_k, cap, d_k), 6), _bits((B, n_v, cap, d_v), 7)
+    kn, vn = _bits((B, T, n_k, d_k), 8), _bits((B, T, n_v, d_v), 9)
+    pos = np.array([8, -3])  # rows 8, 9 fit; 10, 11 and every row of b=1 do not
+    _say("kv_append out-of-range rows")
+    k, v = to_dev(kc, "bf16"), to_dev(vc, "bf16")
+    dq.kv_append(to_dev(kn, "bf16"), to_dev(vn, "bf16"), ints_to_dev(pos), k, v, n_q=2)
+    torch.cuda.synchronize()
+    ek, ev = oracle.kv_append(kc[:1], vc[:1], kn[:1, :2], vn[:1, :2], pos[:1])
+    gk, gv = raw_host(k), raw_host(v)
+    np.testing.assert_array_equal(gk[:1], ek)
+    np.testing.assert_array_equal(gv[:1], ev)
+    np.testing.assert_array_equal(gk[1], kc[1])
+    np.testing.assert_array_equal(gv[1], vc[1])
+
+
+# ------------------------------------------------------------------- prefill
+
+def run_prefill(case):
+    q, k, v, ctx = upload(case)
+    lse = torch.empty((case.batch, case.t_new, case.n_q), dtype=torch.float32, device="cuda")
+    out, lse = dq.prefill(q, k, v, ctx, scale=case.scale, lse=lse)
+    torch.cuda.synchronize()
+    return to_host(out), to_host(lse)
+
+
+PREFILL = [
+    # n_q, n_k, n_v, d_k, d_v, t_new, lengths (after append), l_cap
+    (16, 4, 16, 64, 128, 200, [700, 200], 704),
+    (16, 4, 16, 64, 128, 128, [4000], 4000),
+    (32, 4, 16, 64, 64, 70, [333], 340),
+    (16, 16, 16, 128, 128, 129, [600], 640),
+    (8, 2, 8, 128, 64, 256, [1000, 300], 1024),
+]
+
+
+@pytest.mark.parametrize("cfg", PREFILL, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}-{c[3]}x{c[4]}-t{c[5]}")
+def test_prefill_small_matches_oracle(cfg):
+    n_q, n_k, n_v, d_k, d_v, T, lens, cap = cfg
+    case = synth.make_case(202, dtype="bf16", batch=len(lens), n_q=n_q, n_k=n_k, n_v=n_v,
+                           d_k=d_k, d_v=d_v, ctx_len=lens, l_cap=cap, t_new=T,
+                           poison_tail=True)
+    _say("prefill small", cfg)
+    got, lse = run_prefill(case)
+    q, k, v = case.widened()
+    ref, ref_lse = oracle.prefill(q, k, v, case.ctx_len, case.scale)
+    err = assert_close(got, ref, "bf16", str(cfg))
+    assert_lse_close(lse, ref_lse, "bf16", str(cfg))
+    _say(f"prefill {cfg} normwise rel err {err:.2e}")
+
+
+def test_prefill_rows_without_visible_keys():
+    # ctx_len < t_new: the first t_new - ctx_len rows see nothing.
+    case = synth.make_case(203, dtype="bf16", batch=1, n_q=8, n_k=2, n_v=8, d_k=64, d_v=128,
+                           ctx_len=[50], l_cap=64, t_new=80, poison_tail=True)
+    _say("prefill rows without keys")
+    got, lse = run_prefill(case)
+    assert (got[0, :30] == 0).all() and np.isneginf(lse[0, :30]).all()
+    q, k, v = case.widened()
+    ref, ref_lse = oracle.prefill(q, k, v, case.ctx_len, case.scale,
+                                  rows=[(0, r) for r in range(30, 80)])
+    assert_close(got[0, 30:], ref[0, 30:], "bf16", "rows with keys")
+    assert_lse_close(lse[0, 30:], ref_lse[0, 30:], "bf16", "rows with keys")
+
+
+def test_prefill_full_workload_sampled_rows():
+    case = synth.make_case(**synth.workload("prefill2k_on_30k"))
+    _say("prefill full workload 2048 on 30720")
+    got, lse = run_prefill(case)
+    rows = [0, 1, 31, 32, 127, 128, 129, 1000, 1023, 1024, 2000, 2046, 2047]
+    q, k, v = case.widened()
+    ref, ref_lse = oracle.prefill(q, k, v, case.ctx_len, case.scale,
+                                  rows=[(0, r) for r in rows])
+    err = assert_close(got[0, rows], ref[0, rows], "bf16", "prefill full")
+    assert_lse_close(lse[0, rows], ref_lse[0, rows], "bf16", "prefill full")
+    _say(f"prefill full normwise rel err {err:.2e} on {len(rows)} rows")
+    # Property at every row: no NaN, and lse grows with the visible length
+    # only through the scores (finite everywhere).
+    assert np.isfinite(got).all() and np.isfinite(lse).all()
+
+
+def test_prefill_last_row_matches_decode():
+    case = synth.make_case(204, dtype="bf16", batch=2, n_q=16, n_k=4, n_v=16, d_k=64, d_v=128,
+                           ctx_len=[3000, 2500], l_cap=3008, t_new=64)
+    _say("prefill last row vs decode")
+    got, _ = run_prefill(case)
+    q, k, v, ctx = upload(case)
+    out, _ = dq.decode(q[:, -1].contiguous(), k, v, ctx, scale=case.scale)
+    torch.cuda.synchronize()
+    dec = to_host(out)
+    assert_close(got[:, -1], dec, "bf16", "last row")
