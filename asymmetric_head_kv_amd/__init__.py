@@ -41,7 +41,8 @@ SIGNATURES = {
     "kv_append": (_i32, [_i32] * 9 + [_vp] * 6),
     "diffqkv_decode": (_i32, [_i32] * 9 + [_f32] + [_vp] * 6 + [_i32, _vp, _sz, _vp]),
     "diffqkv_prefill": (_i32, [_i32] * 9 + [_f32] + [_vp] * 7),
-    "diffqkv_decode_split": (_i32, [_i32] * 9 + [_f32] + [_vp] * 4 + [_i32, _vp, _sz, _vp]),
+    "diffqkv_decode_split": (_i32, [_i32] * 9 + [_f32] + [_vp] * 6 + [_i32, _vp, _sz, _vp]),
+    "diffqkv_decode_append": (_i32, [_i32] * 9 + [_f32] + [_vp] * 8 + [_i32, _vp, _sz, _vp]),
     "diffqkv_decode_combine": (_i32, [_i32] * 9 + [_vp] * 3 + [_i32, _vp, _sz, _vp]),
 }
 
@@ -151,9 +152,13 @@ def kv_append(k_new, v_new, pos, k_cache, v_cache, *, n_q=None, stream=None):
 
 
 def decode(q, k_cache, v_cache, ctx_len, *, max_ctx=None, scale=None, out=None,
-           lse=None, chunk_tokens=0, workspace=None, stream=None):
-    """One decode step; returns (out [B, n_q, d_v], lse [B, n_q] or None)."""
-    _device_tensors(q, k_cache, v_cache, ctx_len, out, lse, workspace)
+           lse=None, chunk_tokens=0, workspace=None, k_new=None, v_new=None,
+           stream=None):
+    """One decode step; returns (out [B, n_q, d_v], lse [B, n_q] or None).
+
+    With k_new [B, n_k, d_k] / v_new [B, n_v, d_v] the step first appends
+    them at cache row ctx_len[b] - 1 (diffqkv_decode_append)."""
+    _device_tensors(q, k_cache, v_cache, ctx_len, out, lse, workspace, k_new, v_new)
     B, n_q, d_k = q.shape
     n_k, l_cap = k_cache.shape[1], k_cache.shape[2]
     n_v, d_v = v_cache.shape[1], v_cache.shape[3]
@@ -161,9 +166,13 @@ def decode(q, k_cache, v_cache, ctx_len, *, max_ctx=None, scale=None, out=None,
         raise ValueError("inconsistent q / cache shapes")
     if ctx_len.dtype != torch.int32 or ctx_len.numel() != B:
         raise ValueError("ctx_len must be int32 [B]")
-    for t in (k_cache, v_cache):
-        if t.dtype != q.dtype:
-            raise TypeError("q and the caches must share one dtype")
+    for t in (k_cache, v_cache, k_new, v_new):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError("q, the caches and the new rows must share one dtype")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None and (k_new.numel() != B * n_k * d_k or v_new.numel() != B * n_v * d_v):
+        raise ValueError("k_new must hold [B, n_k, d_k] and v_new [B, n_v, d_v]")
     max_ctx = l_cap if max_ctx is None else int(max_ctx)
     scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
     if out is None:
@@ -175,11 +184,18 @@ def decode(q, k_cache, v_cache, ctx_len, *, max_ctx=None, scale=None, out=None,
     need = decode_workspace_bytes(n_q, n_k, n_v, d_k, d_v, B, max_ctx, chunk_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _check("diffqkv_decode", load().diffqkv_decode(
-        n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, l_cap, max_ctx, scale,
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(out), _ptr(lse),
-        int(chunk_tokens), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if k_new is None:
+        _check("diffqkv_decode", load().diffqkv_decode(
+            n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, l_cap, max_ctx, scale,
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(out), _ptr(lse),
+            int(chunk_tokens), _ptr(workspace), ws_bytes, _stream(stream)))
+    else:
+        _check("diffqkv_decode_append", load().diffqkv_decode_append(
+            n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, l_cap, max_ctx, scale,
+            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
+            _ptr(out), _ptr(lse), int(chunk_tokens), _ptr(workspace), ws_bytes,
+            _stream(stream)))
     return out, lse
 
 

@@ -170,6 +170,7 @@ static int prepare_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, in
   a->S = S; a->C = C; a->scale = scale;
   a->q = q; a->k_cache = k_cache; a->v_cache = v_cache; a->ctx_len = ctx_len;
   a->out = out; a->lse = lse;
+  a->k_new = nullptr; a->v_new = nullptr;
   const size_t parts = (size_t)batch * n_q * C;
   a->part_ml = (float*)workspace;
   a->part_acc = (float*)((char*)workspace + align256(parts * 2 * sizeof(float)));
@@ -199,20 +200,49 @@ int32_t diffqkv_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32
 
 int32_t diffqkv_decode_split(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
                              int32_t dtype, int32_t batch, int32_t l_cap, int32_t max_ctx,
-                             float scale, const void* q, const void* k_cache,
-                             const void* v_cache, const int32_t* ctx_len,
-                             int32_t chunk_tokens, void* workspace,
+                             float scale, const void* q, const void* k_new,
+                             const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* ctx_len, int32_t chunk_tokens, void* workspace,
                              size_t workspace_bytes_given, void* stream) {
+  if (batch == 0 && n_q > 0) {
+    int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+    return st ? st : check_dtype_dims(dtype, d_k, d_v);
+  }
+  if ((k_new == nullptr) != (v_new == nullptr)) return DQKV_ERR_NULL;
+  dqkv::DecodeArgs a;
+  int st = prepare_decode(n_q, n_k, n_v, d_k, d_v, dtype, batch, l_cap, max_ctx, scale, q,
+                          k_cache, v_cache, ctx_len, nullptr, nullptr, chunk_tokens,
+                          workspace, workspace_bytes_given, stream, true, false, &a);
+  if (st) return st;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return DQKV_ERR_ALIGN;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  return to_status(dqkv::launch_decode_split(a));
+}
+
+int32_t diffqkv_decode_append(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                              int32_t d_v, int32_t dtype, int32_t batch, int32_t l_cap,
+                              int32_t max_ctx, float scale, const void* q,
+                              const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, const int32_t* ctx_len, void* out, float* lse,
+                              int32_t chunk_tokens, void* workspace,
+                              size_t workspace_bytes_given, void* stream) {
   if (batch == 0 && n_q > 0) {
     int st = check_heads(n_q, n_k, n_v, d_k, d_v);
     return st ? st : check_dtype_dims(dtype, d_k, d_v);
   }
   dqkv::DecodeArgs a;
   int st = prepare_decode(n_q, n_k, n_v, d_k, d_v, dtype, batch, l_cap, max_ctx, scale, q,
-                          k_cache, v_cache, ctx_len, nullptr, nullptr, chunk_tokens,
-                          workspace, workspace_bytes_given, stream, true, false, &a);
+                          k_cache, v_cache, ctx_len, out, lse, chunk_tokens, workspace,
+                          workspace_bytes_given, stream, true, true, &a);
   if (st) return st;
-  return to_status(dqkv::launch_decode_split(a));
+  if (!k_new || !v_new) return DQKV_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return DQKV_ERR_ALIGN;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  st = to_status(dqkv::launch_decode_split(a));
+  if (st) return st;
+  return to_status(dqkv::launch_decode_combine(a));
 }
 
 int32_t diffqkv_decode_combine(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,

@@ -39,10 +39,14 @@ constexpr int kTile = 64;  // rows per wave iteration: one score per lane
 
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_split_kernel(
-    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const T* __restrict__ q, const T* kc, const T* vc,
     const int32_t* __restrict__ ctx_len, float* __restrict__ part_ml,
     float* __restrict__ part_acc, int n_q, int n_k, int n_v, int l_cap,
-    int max_ctx, int S, int C, float qscale) {
+    int max_ctx, int S, int C, float qscale, const T* __restrict__ k_new,
+    const T* __restrict__ v_new, T* kc_w, T* vc_w) {
+  // kc / kc_w (and vc / vc_w) are the same cache: the kernel reads rows
+  // other than the appended one through the first and writes only that row
+  // through the second.
   constexpr int EPL = Elem<T>::kPer16;       // elements per 16-byte lane load
   constexpr int LPR_K = DK / EPL;            // lanes per K row
   constexpr int RPL_K = 64 / LPR_K;          // K rows per wave load
@@ -76,6 +80,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int vl = lane % LPR_V, vr = lane / LPR_V;
   const T* vp = vc + (((size_t)b * n_v + hv) * l_cap + j0) * DV + vl * EPL;
 
+  // Fused append: the sequence's newest row (L - 1) is read from k_new /
+  // v_new instead of the cache, and written to the cache by one wave per
+  // K head and per V head.  Only this chunk touches row L - 1.
+  const bool fused = k_new != nullptr;
+  const int r_new = fused ? L - 1 - j0 : -1;  // in [0, rows) iff this chunk owns it
+  const T* kn = fused ? k_new + ((size_t)b * n_k + hk) * DK + kl * EPL : nullptr;
+  const T* vn = fused ? v_new + ((size_t)b * n_v + hv) * DV + vl * EPL : nullptr;
+  if (fused && r_new < rows) {
+    if (i % (n_q / n_k) == 0 && lane < LPR_K)
+      *reinterpret_cast<u32x4*>(kc_w + (((size_t)b * n_k + hk) * l_cap + L - 1) * DK + kl * EPL) =
+          load16(kn);
+    if (i % (n_q / n_v) == 0 && lane < LPR_V)
+      *reinterpret_cast<u32x4*>(vc_w + (((size_t)b * n_v + hv) * l_cap + L - 1) * DV + vl * EPL) =
+          load16(vn);
+  }
+
   // The lane keeps the score of tile row my_row = kl * RPL_K + kr (K load kl,
   // row kr of that load); row r's score therefore sits in lane
   // (r % RPL_K) * LPR_K + r / RPL_K.
@@ -86,20 +106,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 
-  for (int t0 = 0; t0 < rows; t0 += kTile) {
-    // Issue the tile's K loads and the first VB V loads together.
-    u32x4 kv[NK], vv[VB];
-#pragma unroll
-    for (int u = 0; u < NK; ++u) {
-      const int r = t0 + u * RPL_K + kr;
-      kv[u] = r < rows ? load16(kp + (size_t)r * DK) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < VB; ++u) {
-      const int r = t0 + u * RPL_V + vr;
-      vv[u] = r < rows ? load16(vp + (size_t)r * DV) : u32x4{0u, 0u, 0u, 0u};
-    }
-
+  auto load_k = [&](int r) -> u32x4 {
+    if (r >= rows) return u32x4{0u, 0u, 0u, 0u};
+    return load16(r == r_new ? kn : kp + (size_t)r * DK);
+  };
+  auto load_v = [&](int r) -> u32x4 {
+    if (r >= rows) return u32x4{0u, 0u, 0u, 0u};
+    return r == r_new ? load16(vn) : load16_nt(vp + (size_t)r * DV);
+  };
+  // Scores of the tile at t0 from its K loads; online-softmax update.
+  // Returns this lane's probability (of row my_row).
+  auto scores = [&](int t0, const u32x4 (&kv)[NK]) -> float {
     float s_mine = 0.f;
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
@@ -112,7 +129,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       s_mine = (u == kl) ? s : s_mine;
     }
     if (t0 + my_row >= rows) s_mine = -INFINITY;
-
     const float m_new = fmaxf(m_run, wave_max(s_mine));
     const float p = fast_exp2(s_mine - m_new);
     const float alpha = fast_exp2(m_run - m_new);
@@ -120,15 +136,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     m_run = m_new;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+    return p;
+  };
 
+  // One tile of 64 rows per iteration: all of its K loads and the first VB
+  // V loads are issued together, the scores wait only for K.  (Holding a
+  // second tile in registers costs occupancy and measured slower.)
+  for (int t0 = 0; t0 < rows; t0 += kTile) {
+    u32x4 kv[NK], vv[VB];
+#pragma unroll
+    for (int u = 0; u < NK; ++u) kv[u] = load_k(t0 + u * RPL_K + kr);
+#pragma unroll
+    for (int u = 0; u < VB; ++u) vv[u] = load_v(t0 + u * RPL_V + vr);
+    const float p = scores(t0, kv);
 #pragma unroll
     for (int vb = 0; vb < NV; vb += VB) {
       if (vb > 0) {  // only for fp32 with wide V rows: next batch of loads
 #pragma unroll
-        for (int u = 0; u < VB; ++u) {
-          const int r = t0 + (vb + u) * RPL_V + vr;
-          vv[u] = r < rows ? load16(vp + (size_t)r * DV) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int u = 0; u < VB; ++u) vv[u] = load_v(t0 + (vb + u) * RPL_V + vr);
       }
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
@@ -161,82 +186,78 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 }
 
 constexpr int kCombineThreads = 256;
+constexpr int kCombineCols = 32;  // value columns per combine workgroup
 
+// One workgroup per (query head, sequence, 32-column slice of d_v).  Every
+// partial the workgroup needs is requested before any is used, so the merge
+// costs one memory round trip; the (m, l) pairs are re-read by each slice.
 template <typename T, int DV>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_acc,
     const int32_t* __restrict__ ctx_len, T* __restrict__ out,
     float* __restrict__ lse, int n_q, int l_cap, int max_ctx, int S, int C) {
-  constexpr int LPR = DV / 4;                 // lanes per partial row (float4)
+  constexpr int COLS = DV < kCombineCols ? DV : kCombineCols;
+  constexpr int LPR = COLS / 4;               // lanes per partial row slice (float4)
   constexpr int CPP = kCombineThreads / LPR;  // partials per pass
-  static_assert(LPR <= kCombineThreads, "d_v");
-  extern __shared__ float smem[];
-  float* w_s = smem;                      // [C] chunk weights
-  float* red_s = smem + ((C + 3) & ~3);   // [CPP][DV] partial sums (16-byte aligned)
-  __shared__ float wred[kCombineThreads / 64];
+  constexpr int U = 4;                        // passes whose loads are in flight together
+  __shared__ float red[kCombineThreads / 64];
+  __shared__ f32x4 part[CPP][LPR];
 
-  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int i = blockIdx.x, b = blockIdx.y, slice = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int L = ctx_len[b];
   L = max(0, min(L, min(max_ctx, l_cap)));
   const int nc = min(C, (L + S - 1) / S);
   const size_t base = ((size_t)b * n_q + i) * C;
+  const int cl = tid % LPR, cr = tid / LPR;
+  const float* src = part_acc + base * DV + slice * COLS + cl * 4;
 
+  // Issue the first U passes of partial loads and this thread's (m, l).
+  f32x4 a[U];
+  float mc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = cr + u * CPP;
+    a[u] = c < nc ? *reinterpret_cast<const f32x4*>(src + (size_t)c * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
+    mc[u] = c < nc ? part_ml[2 * (base + c)] : -INFINITY;
+  }
+  // Global max over all chunks.
   float M = -INFINITY;
   for (int c = tid; c < nc; c += kCombineThreads) M = fmaxf(M, part_ml[2 * (base + c)]);
   M = wave_max(M);
-  if (lane == 0) wred[wave] = M;
+  if (lane == 0) red[wave] = M;
   __syncthreads();
-  M = wred[0];
-#pragma unroll
-  for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, wred[w]);
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
-
+  // Denominator Lambda = sum_c 2^(m_c - M) l_c.
   float lam = 0.f;
-  for (int c = tid; c < nc; c += kCombineThreads) {
-    const float w = fast_exp2(part_ml[2 * (base + c)] - M);
-    w_s[c] = w;
-    lam += w * part_ml[2 * (base + c) + 1];
-  }
+  for (int c = tid; c < nc; c += kCombineThreads)
+    lam += fast_exp2(part_ml[2 * (base + c)] - M) * part_ml[2 * (base + c) + 1];
   lam = wave_sum(lam);
-  if (lane == 0) wred[wave] = lam;
-  __syncthreads();
-  lam = 0.f;
-#pragma unroll
-  for (int w = 0; w < kCombineThreads / 64; ++w) lam += wred[w];
+  if (lane == 0) red[wave] = lam;
 
-  const int cl = tid % LPR, cr = tid / LPR;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  const float* src = part_acc + base * DV + cl * 4;
-  int c = cr;
-  for (; c + 3 * CPP < nc; c += 4 * CPP) {
-    const f32x4 a0 = *reinterpret_cast<const f32x4*>(src + (size_t)c * DV);
-    const f32x4 a1 = *reinterpret_cast<const f32x4*>(src + (size_t)(c + CPP) * DV);
-    const f32x4 a2 = *reinterpret_cast<const f32x4*>(src + (size_t)(c + 2 * CPP) * DV);
-    const f32x4 a3 = *reinterpret_cast<const f32x4*>(src + (size_t)(c + 3 * CPP) * DV);
-    o += w_s[c] * a0;
-    o += w_s[c + CPP] * a1;
-    o += w_s[c + 2 * CPP] * a2;
-    o += w_s[c + 3 * CPP] * a3;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float w = cr + u * CPP < nc ? fast_exp2(mc[u] - M) : 0.f;
+    o += w * a[u];
   }
-  for (; c < nc; c += CPP) o += w_s[c] * *reinterpret_cast<const f32x4*>(src + (size_t)c * DV);
-
-  if (CPP > 1) {
-    *reinterpret_cast<f32x4*>(red_s + cr * DV + cl * 4) = o;
-    __syncthreads();
-    if (cr == 0) {
-      for (int k = 1; k < CPP; ++k) o += *reinterpret_cast<const f32x4*>(red_s + k * DV + cl * 4);
-    }
-  }
-  if (cr == 0) {
+  for (int c = cr + U * CPP; c < nc; c += CPP)
+    o += fast_exp2(part_ml[2 * (base + c)] - M) * *reinterpret_cast<const f32x4*>(src + (size_t)c * DV);
+  part[cr][cl] = o;
+  __syncthreads();
+  lam = red[0] + red[1] + red[2] + red[3];
+  if (tid < LPR) {
+    f32x4 t = part[0][tid];
+    for (int k = 1; k < CPP; ++k) t += part[k][tid];
     const float inv = nc > 0 ? 1.f / lam : 0.f;
-    T* dst = out + ((size_t)b * n_q + i) * DV + cl * 4;
-    dst[0] = Elem<T>::from_f32(o.x * inv);
-    dst[1] = Elem<T>::from_f32(o.y * inv);
-    dst[2] = Elem<T>::from_f32(o.z * inv);
-    dst[3] = Elem<T>::from_f32(o.w * inv);
+    T* dst = out + ((size_t)b * n_q + i) * DV + slice * COLS + tid * 4;
+    dst[0] = Elem<T>::from_f32(t.x * inv);
+    dst[1] = Elem<T>::from_f32(t.y * inv);
+    dst[2] = Elem<T>::from_f32(t.z * inv);
+    dst[3] = Elem<T>::from_f32(t.w * inv);
   }
-  if (tid == 0 && lse != nullptr)
+  if (tid == 0 && slice == 0 && lse != nullptr)
     lse[(size_t)b * n_q + i] = nc > 0 ? (M + fast_log2(lam)) * kLn2 : -INFINITY;
 }
 
@@ -249,18 +270,18 @@ static hipError_t launch_split_t(const DecodeArgs& a) {
   hipLaunchKernelGGL((decode_split_kernel<T, DK, DV>), grid, dim3(256), 0, a.stream,
                      (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.ctx_len,
                      a.part_ml, a.part_acc, a.n_q, a.n_k, a.n_v, a.l_cap, a.max_ctx, a.S,
-                     a.C, qscale);
+                     a.C, qscale, (const T*)a.k_new, (const T*)a.v_new, (T*)a.k_cache,
+                     (T*)a.v_cache);
   return hipGetLastError();
 }
 
 template <typename T, int DV>
 static hipError_t launch_combine_t(const DecodeArgs& a) {
-  constexpr int CPP = kCombineThreads / (DV / 4);
-  const size_t lds = ((size_t)((a.C + 3) & ~3) + (size_t)CPP * DV) * sizeof(float);
-  dim3 grid(a.n_q, a.batch);
-  hipLaunchKernelGGL((decode_combine_kernel<T, DV>), grid, dim3(kCombineThreads), lds,
-                     a.stream, a.part_ml, a.part_acc, a.ctx_len, (T*)a.out, a.lse, a.n_q,
-                     a.l_cap, a.max_ctx, a.S, a.C);
+  constexpr int COLS = DV < kCombineCols ? DV : kCombineCols;
+  dim3 grid(a.n_q, a.batch, DV / COLS);
+  hipLaunchKernelGGL((decode_combine_kernel<T, DV>), grid, dim3(kCombineThreads), 0, a.stream,
+                     a.part_ml, a.part_acc, a.ctx_len, (T*)a.out, a.lse, a.n_q, a.l_cap,
+                     a.max_ctx, a.S, a.C);
   return hipGetLastError();
 }
 

@@ -52,6 +52,12 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Streaming load: the nontemporal hint tells the caches the line is read
+// once, which lets long sequential reads run closer to HBM bandwidth.
+__device__ __forceinline__ u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // ---------------------------------------------------------------- DPP
 // dpp_ctrl encodings (GCN/CDNA): quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
 // row_half_mirror (reverse 8 lanes) = 0x141, row_mirror (reverse 16) = 0x140.

@@ -22,6 +22,8 @@ struct DecodeArgs {
   float* lse;
   float* part_ml;   // [B][n_q][C][2]
   float* part_acc;  // [B][n_q][C][d_v]
+  const void* k_new;  // fused append: newest row per sequence, or null
+  const void* v_new;
   hipStream_t stream;
 };
 

@@ -1,18 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the DiffQKV decode hot path on one MI355X.
 
-One step = one decode step of the workload: kv_append of the newest K/V row
-of every sequence, then the split-KV decode kernel, then the combine kernel
-(the path's store, split and combine steps).  Inputs are seeded synthetic
+One step = one decode step of the workload: the newest K/V row of every
+sequence is appended to the caches and attended together with the earlier
+rows (the path's store, split and combine steps; the append is fused into the
+split kernel, so a step is two kernels).  Inputs are seeded synthetic
 caches, resident in HBM before timing starts.  Each step attends a different
 replica of the caches (standing for successive layers) so that the replicas
 together exceed the 256 MB Infinity Cache several times over and the timing
 reflects HBM, not the last-level cache.
 
 The timed steps are captured once in a HIP graph and replayed (the launch
-rate of three small kernels from Python would otherwise bound the step);
-a second, eager pass brackets every kernel with events on the launch stream
-for the per-kernel durations the roofline uses.
+rate from Python would otherwise bound the step).  The roofline's kernel
+duration comes from a graph of that kernel alone, timed the same way.  HBM
+traffic per launch is read from the committed rocprofv3 counter summary in
+profiles/ when that summary was taken from the current kernel source.
 
 Prints one JSON line.  ``value`` is the algorithmic HBM bytes of a step
 (sum over sequences of ctx_len * (n_k d_k + n_v d_v) * element size, plus q,
@@ -58,6 +60,9 @@ def parse():
     p.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     p.add_argument("--kernel-only", action="store_true",
                    help="only run steps (for profilers); skip twin, prefill, CPU baseline")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device copy of BYTES bytes three times (calibrates "
+                        "the HBM byte counters of a profiler) and exit")
     return p.parse_args()
 
 
@@ -134,6 +139,7 @@ class DecodeBench:
         return self.torch.cuda.current_stream().cuda_stream
 
     def append(self, r):
+        """Standalone kv_append of the step's new rows (not part of a step)."""
         k, v = self.caches[r]
         st = self.lib.kv_append(*self.shape, self.dtype_code, self.B, 1, self.l_cap,
                                 self.k_new.data_ptr(), self.v_new.data_ptr(),
@@ -142,11 +148,13 @@ class DecodeBench:
         assert st == 0, st
 
     def split(self, r):
+        """Split kernel with the fused append of the newest row."""
         k, v = self.caches[r]
         st = self.lib.diffqkv_decode_split(
             *self.shape, self.dtype_code, self.B, self.l_cap, self.max_ctx, self.case.scale,
-            self.q.data_ptr(), k.data_ptr(), v.data_ptr(), self.ctx_t.data_ptr(), self.chunk,
-            self.ws.data_ptr(), self.ws_bytes, self._stream())
+            self.q.data_ptr(), self.k_new.data_ptr(), self.v_new.data_ptr(), k.data_ptr(),
+            v.data_ptr(), self.ctx_t.data_ptr(), self.chunk, self.ws.data_ptr(),
+            self.ws_bytes, self._stream())
         assert st == 0, st
 
     def combine(self):
@@ -157,7 +165,6 @@ class DecodeBench:
         assert st == 0, st
 
     def step(self, r):
-        self.append(r)
         self.split(r)
         self.combine()
 
@@ -174,16 +181,7 @@ class DecodeBench:
         if not eager:
             try:
                 for n in {R, steps % R} - {0}:
-                    g = torch.cuda.CUDAGraph()
-                    s = torch.cuda.Stream()
-                    s.wait_stream(torch.cuda.current_stream())
-                    with torch.cuda.stream(s):
-                        self.step(0)
-                    torch.cuda.current_stream().wait_stream(s)
-                    with torch.cuda.graph(g):
-                        for r in range(n):
-                            self.step(r)
-                    graphs[n] = g
+                    graphs[n] = self._graph(self.step, n)
                 for g in graphs.values():  # warm replays
                     g.replay()
                 torch.cuda.synchronize()
@@ -205,31 +203,77 @@ class DecodeBench:
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps, bool(graphs)
 
+    def _graph(self, fn, n):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(s)
+        with torch.cuda.graph(g):
+            for r in range(n):
+                fn(r)
+        return g
+
     def time_kernels(self, steps: int):
-        """Per-kernel average durations (ms) from events on the launch stream."""
+        """Average duration (ms) of the split kernel and of the combine kernel,
+        each timed alone: a graph of back-to-back launches of that kernel over
+        the cache replicas, replayed between two events on the launch stream."""
         torch = self.torch
         R = self.replicas
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-        torch.cuda.synchronize()
-        for s in range(steps):
-            e = ev[s]
-            e[0].record()
-            self.append(s % R)
-            e[1].record()
-            self.split(s % R)
-            e[2].record()
-            self.combine()
-            e[3].record()
-        torch.cuda.synchronize()
-        tot = [0.0, 0.0, 0.0]
-        for e in ev:
-            for k in range(3):
-                tot[k] += e[k].elapsed_time(e[k + 1])
-        return [t / steps for t in tot]
+        out = []
+        for fn in (self.split, lambda r: self.combine()):
+            g = self._graph(fn, R)
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, steps // R)
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(reps):
+                g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            out.append(t0.elapsed_time(t1) / (reps * R))
+        return out
 
     def free(self):
         self.caches = None
         self.torch.cuda.empty_cache()
+
+
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_split_kernel_{}_pmc.txt")
+KERNEL_SOURCES = ("asymmetric_head_kv_amd/csrc/decode.hip",
+                  "asymmetric_head_kv_amd/csrc/device_common.h")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(workload: str):
+    """HBM bytes per split launch from the committed counter summary, or
+    None when there is none or it was taken from other kernel sources."""
+    path = PMC_SUMMARY.format(workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def prefill_bench(steps: int = 10):
@@ -328,6 +372,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        a = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": a.numel() * 4, "copies": 3}))
+        return
 
     log(f"workload {args.workload}: building inputs")
     bench = DecodeBench(args.workload, args.chunk)
@@ -335,8 +387,9 @@ def main():
     ms, graphed = bench.time_steps(args.steps, args.warmup, args.eager)
     log(f"step {ms * 1e3:.2f} us ({'graph' if graphed else 'eager'})")
     k_ms = bench.time_kernels(args.steps)
-    log("kernels (us): append %.2f split %.2f combine %.2f" % tuple(x * 1e3 for x in k_ms))
-    split_gbs = bench.alg_bytes_split / (k_ms[1] * 1e-3) / 1e9
+    log("kernels (us): split %.2f combine %.2f" % tuple(x * 1e3 for x in k_ms))
+    traffic = pmc_traffic(args.workload)
+    split_gbs = bench.alg_bytes_split / (k_ms[0] * 1e-3) / 1e9
     value = bench.alg_bytes_step / (ms * 1e-3) / 1e9
     n_q, n_k, n_v, d_k, d_v = bench.shape
     result = {
@@ -349,14 +402,16 @@ def main():
                    "n_q": n_q, "n_k": n_k, "n_v": n_v, "d_k": d_k, "d_v": d_v,
                    "chunk_rows": bench.S, "cache_replicas": bench.replicas,
                    "timing": "hip graph replay" if graphed else "eager launches",
-                   "step": "kv_append(1 row/seq) + split + combine"},
+                   "step": "split with fused kv_append (1 row/seq) + combine"},
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel",
                      "achieved": round(split_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, scaled)",
                      "alg_bytes_per_launch": bench.alg_bytes_split,
-                     "avg_launch_us": round(k_ms[1] * 1e3, 2)},
-        "kernels_us": {"kv_append": round(k_ms[0] * 1e3, 2), "split": round(k_ms[1] * 1e3, 2),
-                       "combine": round(k_ms[2] * 1e3, 2)},
+                     "avg_launch_us": round(k_ms[0] * 1e3, 2)},
+        "kernels_us": {"split_with_append": round(k_ms[0] * 1e3, 2),
+                       "combine": round(k_ms[1] * 1e3, 2)},
+        "kernel_source_sha256": kernel_source_hash(),
     }
     sym_name = None if args.no_twin else (args.twin or TWINS.get(args.workload))
     asym_bytes = bench.alg_bytes_step

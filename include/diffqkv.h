@@ -36,7 +36,7 @@
  * scores, always fp32, optional (NULL to skip).
  *
  * Supported sizes: 1 <= n_k <= n_q, 1 <= n_v <= n_q, n_q a multiple of n_k
- * and of n_v, n_q / n_k <= 16; d_k, d_v in {32, 64, 128, 256} (prefill: d_k
+ * and of n_v; d_k, d_v in {32, 64, 128, 256}, d_k = 256 bf16 only (prefill: d_k
  * in {64, 128}, d_v in {64, 128}, bf16 only).  Every device pointer must be
  * 16-byte aligned.
  *
@@ -135,21 +135,45 @@ int32_t diffqkv_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * diffqkv_decode_append -- one decode step that first appends the step's
+ * new token: k_new[b] ([B][n_k][d_k], i.e. token-major with t_new = 1) and
+ * v_new[b] ([B][n_v][d_v]) are written to cache row ctx_len[b] - 1 (so
+ * ctx_len counts rows after the append, Step 2 of section 3.4), and every
+ * query head then attends rows 0 .. ctx_len[b] - 1 as in diffqkv_decode.
+ * Same result, bit for bit, as kv_append with pos[b] = ctx_len[b] - 1
+ * followed by diffqkv_decode, in two kernels instead of three: the split
+ * kernel that owns row ctx_len[b] - 1 reads the new row from k_new / v_new
+ * and stores it.  Requires 1 <= ctx_len[b] <= max_ctx for every b that
+ * should append (ctx_len[b] = 0: nothing appended, out = 0, lse = -inf).
+ */
+int32_t diffqkv_decode_append(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                              int32_t d_v, int32_t dtype, int32_t batch,
+                              int32_t l_cap, int32_t max_ctx, float scale,
+                              const void* q, const void* k_new,
+                              const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* ctx_len, void* out, float* lse,
+                              int32_t chunk_tokens, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * diffqkv_decode_split / diffqkv_decode_combine -- the two halves of
- * diffqkv_decode, for callers that time or schedule them separately (the
- * pages measure the split and combine kernels of FlexHeadFA separately).
- * Arguments have the meaning given for diffqkv_decode; both calls of one
- * step must pass the same sizes, chunk_tokens and workspace.  The split
- * kernel writes every non-empty chunk's (max, sum, weighted V sum) to the
- * workspace; the combine reads them and writes out and lse.
+ * diffqkv_decode (or, with k_new / v_new non-NULL, of diffqkv_decode_append),
+ * for callers that time or schedule them separately: the pages measure the
+ * split and combine kernels of FlexHeadFA separately.  Arguments have the
+ * meaning given above; both calls of one step must pass the same sizes,
+ * chunk_tokens and workspace.  The split kernel writes every non-empty
+ * chunk's (max, sum, weighted V sum) to the workspace; the combine reads
+ * them and writes out and lse.  k_cache / v_cache are written only when
+ * k_new / v_new are given (both or neither).
  */
 int32_t diffqkv_decode_split(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
                              int32_t d_v, int32_t dtype, int32_t batch,
                              int32_t l_cap, int32_t max_ctx, float scale,
-                             const void* q, const void* k_cache,
-                             const void* v_cache, const int32_t* ctx_len,
-                             int32_t chunk_tokens, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             const void* q, const void* k_new,
+                             const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* ctx_len, int32_t chunk_tokens,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 int32_t diffqkv_decode_combine(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
                                int32_t d_v, int32_t dtype, int32_t batch,

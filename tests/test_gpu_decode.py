@@ -139,6 +139,50 @@ def test_kv_group_sharing_equivalence_gpu():
     np.testing.assert_array_equal(la, lb)
 
 
+FUSED = [
+    # dtype, n_q, n_k, n_v, d_k, d_v, lengths after the append, l_cap, chunk
+    ("bf16", 16, 4, 16, 64, 128, [65, 1, 128, 300, 4097], 4100, 0),
+    ("bf16", 16, 4, 16, 64, 128, [65, 1, 128, 300, 4097], 4100, 64),
+    ("bf16", 32, 4, 16, 64, 64, [700, 64], 704, 128),
+    ("bf16", 16, 16, 16, 128, 128, [1000, 999], 1024, 0),
+    ("f32", 8, 2, 4, 32, 64, [257, 2], 260, 64),
+]
+
+
+@pytest.mark.parametrize("cfg", FUSED, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-{c[4]}x{c[5]}-c{c[8]}")
+def test_fused_append_equals_append_then_decode(cfg):
+    dtype, n_q, n_k, n_v, d_k, d_v, lens, cap, chunk = cfg
+    B = len(lens)
+    case = synth.make_case(303, dtype=dtype, batch=B, n_q=n_q, n_k=n_k, n_v=n_v, d_k=d_k,
+                           d_v=d_v, ctx_len=lens, l_cap=cap, poison_tail=True)
+    k_new, v_new = synth.new_rows(303, dtype=dtype, batch=B, t_new=1, n_k=n_k, n_v=n_v,
+                                  d_k=d_k, d_v=d_v)
+    _say("fused append", cfg)
+    lens = np.asarray(lens)
+    # Two-kernel-launch reference: kv_append, then decode.
+    q, k1, v1, ctx = upload(case)
+    kn, vn = to_dev(k_new, dtype), to_dev(v_new, dtype)
+    dq.kv_append(kn, vn, ints_to_dev(lens - 1), k1, v1, n_q=n_q)
+    lse1 = torch.empty((B, n_q), dtype=torch.float32, device="cuda")
+    out1, _ = dq.decode(q, k1, v1, ctx, lse=lse1, chunk_tokens=chunk)
+    # Fused.
+    _, k2, v2, _ = upload(case)
+    lse2 = torch.empty((B, n_q), dtype=torch.float32, device="cuda")
+    out2, _ = dq.decode(q, k2, v2, ctx, lse=lse2, chunk_tokens=chunk,
+                        k_new=kn.view(B, n_k, d_k), v_new=vn.view(B, n_v, d_v))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(raw_host(out2), raw_host(out1))
+    np.testing.assert_array_equal(raw_host(lse2), raw_host(lse1))
+    np.testing.assert_array_equal(raw_host(k2), raw_host(k1))
+    np.testing.assert_array_equal(raw_host(v2), raw_host(v1))
+    # And both match the oracle of Step 2 followed by Steps 3-5.
+    kh, vh = oracle.kv_append(case.k_cache, case.v_cache, k_new, v_new, lens - 1)
+    wid = (lambda a: synth.bf16_bits_to_f32(a)) if dtype == "bf16" else (lambda a: a)
+    ref, ref_lse = oracle.decode(wid(case.q), wid(kh), wid(vh), lens, case.scale)
+    assert_close(to_host(out2), ref, dtype, str(cfg))
+    assert_lse_close(to_host(lse2), ref_lse, dtype, str(cfg))
+
+
 # ------------------------------------------------------------ full workloads
 
 @pytest.mark.parametrize("name", ["decode32k_asym", "decode32k_sym"])
@@ -152,19 +196,24 @@ def test_decode_32k_full(name):
     _say(f"{name} normwise rel err {err:.2e}")
 
 
-def test_ragged_batch_append_then_decode_full():
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "kv_append"])
+def test_ragged_batch_append_then_decode_full(fused):
     kw = synth.workload("ragged16")
     old = np.asarray(kw["ctx_len"])
     case = synth.make_case(**{**kw, "poison_tail": True})
     k_new, v_new = synth.new_rows(kw["seed"], dtype="bf16", batch=16, t_new=1, n_k=4, n_v=16,
                                   d_k=64, d_v=128)
-    _say("ragged16: append + decode, lengths", old.min(), old.max())
+    _say("ragged16: append + decode, fused", fused, "lengths", old.min(), old.max())
     q, k, v, _ = upload(case)
-    pos = ints_to_dev(old)
-    dq.kv_append(to_dev(k_new, "bf16"), to_dev(v_new, "bf16"), pos, k, v, n_q=16)
+    kn, vn = to_dev(k_new, "bf16"), to_dev(v_new, "bf16")
     ctx = ints_to_dev(old + 1)
     lse = torch.empty((16, 16), dtype=torch.float32, device="cuda")
-    out, lse = dq.decode(q, k, v, ctx, max_ctx=case.l_cap, lse=lse)
+    if fused:
+        out, lse = dq.decode(q, k, v, ctx, max_ctx=case.l_cap, lse=lse,
+                             k_new=kn.view(16, 4, 64), v_new=vn.view(16, 16, 128))
+    else:
+        dq.kv_append(kn, vn, ints_to_dev(old), k, v, n_q=16)
+        out, lse = dq.decode(q, k, v, ctx, max_ctx=case.l_cap, lse=lse)
     torch.cuda.synchronize()
     kh, vh = oracle.kv_append(case.k_cache, case.v_cache, k_new, v_new, old)
     np.testing.assert_array_equal(raw_host(k), kh)
