@@ -21,7 +21,8 @@ import os
 import torch
 
 __all__ = ["DQKVError", "lib_path", "load", "decode", "decode_chunk",
-           "decode_workspace_bytes", "prefill", "kv_append", "STATUS"]
+           "decode_workspace_bytes", "prefill", "prefill_workspace_bytes", "kv_append",
+           "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libdiffqkv.so")
@@ -40,7 +41,8 @@ SIGNATURES = {
     "diffqkv_decode_workspace": (_i32, [_i32] * 8 + [ctypes.POINTER(_sz)]),
     "kv_append": (_i32, [_i32] * 9 + [_vp] * 6),
     "diffqkv_decode": (_i32, [_i32] * 9 + [_f32] + [_vp] * 6 + [_i32, _vp, _sz, _vp]),
-    "diffqkv_prefill": (_i32, [_i32] * 9 + [_f32] + [_vp] * 7),
+    "diffqkv_prefill": (_i32, [_i32] * 9 + [_f32] + [_vp] * 7 + [_sz, _vp]),
+    "diffqkv_prefill_workspace": (_i32, [_i32] * 7 + [ctypes.POINTER(_sz)]),
     "diffqkv_decode_split": (_i32, [_i32] * 9 + [_f32] + [_vp] * 6 + [_i32, _vp, _sz, _vp]),
     "diffqkv_decode_append": (_i32, [_i32] * 9 + [_f32] + [_vp] * 8 + [_i32, _vp, _sz, _vp]),
     "diffqkv_decode_combine": (_i32, [_i32] * 9 + [_vp] * 3 + [_i32, _vp, _sz, _vp]),
@@ -199,10 +201,21 @@ def decode(q, k_cache, v_cache, ctx_len, *, max_ctx=None, scale=None, out=None,
     return out, lse
 
 
+def prefill_workspace_bytes(n_q, n_k, n_v, d_k, d_v, batch, t_new) -> int:
+    out = _sz()
+    _check("diffqkv_prefill_workspace",
+           load().diffqkv_prefill_workspace(n_q, n_k, n_v, d_k, d_v, batch, t_new,
+                                            ctypes.byref(out)))
+    return out.value
+
+
 def prefill(q, k_cache, v_cache, ctx_len, *, scale=None, out=None, lse=None,
-            stream=None):
-    """Causal prefill of t_new rows (already appended); returns (out, lse)."""
-    _device_tensors(q, k_cache, v_cache, ctx_len, out, lse)
+            workspace=None, stream=None):
+    """Causal prefill of t_new rows (already appended); returns (out, lse).
+
+    A workspace of prefill_workspace_bytes is allocated when none is given
+    (pass one to avoid the allocation; an empty tensor runs unsplit)."""
+    _device_tensors(q, k_cache, v_cache, ctx_len, out, lse, workspace)
     B, T, n_q, d_k = q.shape
     n_k, l_cap = k_cache.shape[1], k_cache.shape[2]
     n_v, d_v = v_cache.shape[1], v_cache.shape[3]
@@ -217,8 +230,11 @@ def prefill(q, k_cache, v_cache, ctx_len, *, scale=None, out=None, lse=None,
         raise ValueError("out must be [B, t_new, n_q, d_v] in q's dtype")
     if lse is not None and (lse.shape != (B, T, n_q) or lse.dtype != torch.float32):
         raise ValueError("lse must be float32 [B, t_new, n_q]")
+    if workspace is None:
+        need = prefill_workspace_bytes(n_q, n_k, n_v, d_k, d_v, B, T)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check("diffqkv_prefill", load().diffqkv_prefill(
         n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, T, l_cap, scale,
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(out), _ptr(lse),
-        _stream(stream)))
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse

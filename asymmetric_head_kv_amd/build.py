@@ -27,8 +27,17 @@ FLAGS = [
     "-Wall", "-Wno-unused-result",
     # Keep the compiler from forming packed-fp32 VALU instructions.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core results in ordinary VGPRs: the softmax reads them directly
+    # instead of copying them out of accumulation registers every tile.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
+
+
+# Per-source additions.  The prefill kernel's softmax takes row maxima of
+# matrix-core results that are never NaN: with relaxed NaN handling (and the
+# IEEE mode bit off, which that permits) fmaxf needs no operand quieting.
+EXTRA = {"prefill.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _run(cmd):
@@ -47,7 +56,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     jobs = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         for r in ex.map(_run, cmds):

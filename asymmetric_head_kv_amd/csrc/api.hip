@@ -58,6 +58,25 @@ int chunks_for(int max_ctx, int S) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kPrefillRows = 128;  // query rows per prefill workgroup
+
+// Key splits for a prefill: enough workgroups for two per CU (so matrix-core
+// and softmax work of different waves overlap on each SIMD), at most 4.
+int plan_prefill_split(int n_q, int batch, int t_new) {
+  const long long wg = (long long)batch * n_q * ((t_new + kPrefillRows - 1) / kPrefillRows);
+  if (wg <= 0) return 1;
+  long long ns = (2LL * kCUs + wg - 1) / wg;
+  if (ns < 1) ns = 1;
+  if (ns > 4) ns = 4;
+  return (int)ns;
+}
+
+size_t prefill_workspace_bytes(int ns, int n_q, int d_v, int batch, int t_new) {
+  if (ns <= 1) return 0;
+  const size_t rows = (size_t)batch * t_new * n_q;
+  return align256((size_t)ns * rows * d_v * sizeof(float)) + (size_t)ns * rows * sizeof(float);
+}
+
 size_t workspace_bytes(int n_q, int d_v, int batch, int C) {
   const size_t parts = (size_t)batch * n_q * C;
   return align256(parts * 2 * sizeof(float)) + parts * d_v * sizeof(float);
@@ -262,11 +281,23 @@ int32_t diffqkv_decode_combine(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_
   return to_status(dqkv::launch_decode_combine(a));
 }
 
+int32_t diffqkv_prefill_workspace(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                                  int32_t d_v, int32_t batch, int32_t t_new, size_t* bytes) {
+  if (!bytes) return DQKV_ERR_NULL;
+  int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+  if (st) return st;
+  if (batch < 0 || t_new < 0) return DQKV_ERR_SHAPE;
+  const int ns = plan_prefill_split(n_q, batch, t_new);
+  *bytes = prefill_workspace_bytes(ns, n_q, d_v, batch, t_new);
+  return DQKV_OK;
+}
+
 int32_t diffqkv_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
                         int32_t dtype, int32_t batch, int32_t t_new, int32_t l_cap,
                         float scale, const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* ctx_len, void* out,
-                        float* lse, void* stream) {
+                        float* lse, void* workspace, size_t workspace_bytes_given,
+                        void* stream) {
   int st = check_heads(n_q, n_k, n_v, d_k, d_v);
   if (st) return st;
   if (dtype != DQKV_BF16) return DQKV_ERR_UNSUPPORTED;
@@ -275,13 +306,24 @@ int32_t diffqkv_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int3
   if (!(scale > 0.f) || !isfinite(scale)) return DQKV_ERR_SHAPE;
   if (batch == 0 || t_new == 0) return DQKV_OK;
   if (!q || !k_cache || !v_cache || !ctx_len || !out) return DQKV_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (workspace && !aligned16(workspace)))
     return DQKV_ERR_ALIGN;
+  const long long n_qtiles = ((long long)t_new + kPrefillRows - 1) / kPrefillRows;
+  int ns = plan_prefill_split(n_q, batch, t_new);
+  const size_t need = prefill_workspace_bytes(ns, n_q, d_v, batch, t_new);
+  if (ns > 1 && (!workspace || workspace_bytes_given < need)) ns = 1;  // run unsplit
+  if (n_qtiles * n_q * ns > 0x7fffffffLL) return DQKV_ERR_UNSUPPORTED;
   dqkv::PrefillArgs a;
   a.n_q = n_q; a.n_k = n_k; a.n_v = n_v; a.d_k = d_k; a.d_v = d_v;
   a.batch = batch; a.t_new = t_new; a.l_cap = l_cap; a.scale = scale;
   a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.ctx_len = ctx_len;
   a.out = out; a.lse = lse;
+  a.n_split = ns;
+  const size_t rows = (size_t)batch * t_new * n_q;
+  a.part_o = ns > 1 ? (float*)workspace : nullptr;
+  a.part_ml = ns > 1 ? (float*)((char*)workspace + align256((size_t)ns * rows * d_v * sizeof(float)))
+                     : nullptr;
   a.stream = (hipStream_t)stream;
   return to_status(dqkv::launch_prefill(a));
 }

@@ -49,6 +49,9 @@ struct PrefillArgs {
   const int32_t* ctx_len;
   void* out;
   float* lse;
+  int n_split;      // key splits (1: no merge, no workspace)
+  float* part_o;    // [n_split][B][t_new][n_q][d_v] fp32
+  float* part_ml;   // [n_split][B][t_new][n_q] split lse, log2 units
   hipStream_t stream;
 };
 

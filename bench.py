@@ -292,13 +292,16 @@ def prefill_bench(steps: int = 10):
     q, k, v = up(case.q), up(case.k_cache), up(case.v_cache)
     ctx = torch.from_numpy(case.ctx_len.astype(np.int32)).to(dev)
     out = torch.empty((case.batch, case.t_new, case.n_q, case.d_v), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(16, dq.prefill_workspace_bytes(case.n_q, case.n_k, case.n_v, case.d_k,
+                                                        case.d_v, case.batch, case.t_new)),
+                     dtype=torch.uint8, device=dev)
     for _ in range(2):
-        dq.prefill(q, k, v, ctx, out=out)
+        dq.prefill(q, k, v, ctx, out=out, workspace=ws)
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(steps):
-        dq.prefill(q, k, v, ctx, out=out)
+        dq.prefill(q, k, v, ctx, out=out, workspace=ws)
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps

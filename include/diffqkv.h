@@ -193,13 +193,25 @@ int32_t diffqkv_decode_combine(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_
  * of section 3.4 Steps 2-5 applied token by token).  Rows with p < 0 (that
  * is ctx_len[b] < t_new) get out = 0, lse = -inf; ctx_len is clamped to
  * l_cap.
+ *
+ * workspace (optional, 16-byte aligned, contents need not be initialised):
+ * when it holds diffqkv_prefill_workspace bytes and that size is non-zero,
+ * small launches split every row's keys over several workgroups and merge
+ * the parts exactly in log-sum-exp form (one more kernel); with NULL or too
+ * small a workspace the prefill runs unsplit.  Results agree within
+ * rounding either way.
  */
+int32_t diffqkv_prefill_workspace(int32_t n_q, int32_t n_k, int32_t n_v,
+                                  int32_t d_k, int32_t d_v, int32_t batch,
+                                  int32_t t_new, size_t* bytes);
+
 int32_t diffqkv_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
                         int32_t d_v, int32_t dtype, int32_t batch,
                         int32_t t_new, int32_t l_cap, float scale,
                         const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* ctx_len,
-                        void* out, float* lse, void* stream);
+                        void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

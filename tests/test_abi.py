@@ -138,7 +138,7 @@ def test_prefill_validation(lib):
         a.update(kw)
         return lib.diffqkv_prefill(a["n_q"], a["n_k"], a["n_v"], a["d_k"], a["d_v"], a["dtype"],
                                    a["B"], a["T"], a["l_cap"], a["scale"], a["q"], a["kc"],
-                                   a["vc"], a["ctx"], a["out"], a["lse"], None)
+                                   a["vc"], a["ctx"], a["out"], a["lse"], None, 0, None)
     assert call(dtype=0) == UNSUP
     assert call(d_k=32) == UNSUP
     assert call(d_v=256) == UNSUP
@@ -146,6 +146,15 @@ def test_prefill_validation(lib):
     assert call(out=None) == NULL
     assert call(q=FAKE + 2) == ALIGN
     assert call(T=0) == OK
+
+
+def test_prefill_workspace_plan(lib):
+    # 2048 rows x 16 heads = 256 workgroups of 128 rows: two key splits so
+    # that every CU gets two workgroups; large launches run unsplit.
+    need = dq.prefill_workspace_bytes(16, 4, 16, 64, 128, 1, 2048)
+    rows = 2048 * 16
+    assert need == -(-2 * rows * 128 * 4 // 256) * 256 + 2 * rows * 4
+    assert dq.prefill_workspace_bytes(16, 4, 16, 64, 128, 8, 4096) == 0
 
 
 def test_binding_refuses_cpu_tensors(lib):

@@ -74,12 +74,17 @@ def test_kv_append_skips_rows_outside_cache():
 
 # ------------------------------------------------------------------- prefill
 
-def run_prefill(case):
+def run_prefill(case, with_lse=True, split=True):
+    """Prefill on the GPU.  split=False passes an empty workspace (one key
+    split); with_lse=False takes the path that sums the rounded weights."""
     q, k, v, ctx = upload(case)
-    lse = torch.empty((case.batch, case.t_new, case.n_q), dtype=torch.float32, device="cuda")
-    out, lse = dq.prefill(q, k, v, ctx, scale=case.scale, lse=lse)
+    lse = None
+    if with_lse:
+        lse = torch.empty((case.batch, case.t_new, case.n_q), dtype=torch.float32, device="cuda")
+    ws = None if split else torch.empty(0, dtype=torch.uint8, device="cuda")
+    out, lse = dq.prefill(q, k, v, ctx, scale=case.scale, lse=lse, workspace=ws)
     torch.cuda.synchronize()
-    return to_host(out), to_host(lse)
+    return to_host(out), (to_host(lse) if with_lse else None)
 
 
 PREFILL = [
@@ -98,13 +103,15 @@ def test_prefill_small_matches_oracle(cfg):
     case = synth.make_case(202, dtype="bf16", batch=len(lens), n_q=n_q, n_k=n_k, n_v=n_v,
                            d_k=d_k, d_v=d_v, ctx_len=lens, l_cap=cap, t_new=T,
                            poison_tail=True)
-    _say("prefill small", cfg)
-    got, lse = run_prefill(case)
     q, k, v = case.widened()
     ref, ref_lse = oracle.prefill(q, k, v, case.ctx_len, case.scale)
-    err = assert_close(got, ref, "bf16", str(cfg))
-    assert_lse_close(lse, ref_lse, "bf16", str(cfg))
-    _say(f"prefill {cfg} normwise rel err {err:.2e}")
+    for with_lse, split in ((True, True), (False, True), (True, False), (False, False)):
+        _say("prefill small", cfg, "lse" if with_lse else "no lse", "split" if split else "unsplit")
+        got, lse = run_prefill(case, with_lse, split)
+        err = assert_close(got, ref, "bf16", f"{cfg} lse={with_lse} split={split}")
+        if with_lse:
+            assert_lse_close(lse, ref_lse, "bf16", str(cfg))
+        _say(f"prefill {cfg} normwise rel err {err:.2e}")
 
 
 def test_prefill_rows_without_visible_keys():
@@ -112,6 +119,8 @@ def test_prefill_rows_without_visible_keys():
     case = synth.make_case(203, dtype="bf16", batch=1, n_q=8, n_k=2, n_v=8, d_k=64, d_v=128,
                            ctx_len=[50], l_cap=64, t_new=80, poison_tail=True)
     _say("prefill rows without keys")
+    got, _ = run_prefill(case, with_lse=False, split=False)
+    assert (got[0, :30] == 0).all()
     got, lse = run_prefill(case)
     assert (got[0, :30] == 0).all() and np.isneginf(lse[0, :30]).all()
     q, k, v = case.widened()
@@ -123,12 +132,15 @@ def test_prefill_rows_without_visible_keys():
 
 def test_prefill_full_workload_sampled_rows():
     case = synth.make_case(**synth.workload("prefill2k_on_30k"))
-    _say("prefill full workload 2048 on 30720")
-    got, lse = run_prefill(case)
+    _say("prefill full workload 2048 on 30720 (split, as the benchmark runs it)")
+    got, _ = run_prefill(case, with_lse=False)
     rows = [0, 1, 31, 32, 127, 128, 129, 1000, 1023, 1024, 2000, 2046, 2047]
     q, k, v = case.widened()
     ref, ref_lse = oracle.prefill(q, k, v, case.ctx_len, case.scale,
                                   rows=[(0, r) for r in rows])
+    err = assert_close(got[0, rows], ref[0, rows], "bf16", "prefill full, no lse")
+    _say(f"prefill full (no lse) normwise rel err {err:.2e}")
+    got, lse = run_prefill(case)
     err = assert_close(got[0, rows], ref[0, rows], "bf16", "prefill full")
     assert_lse_close(lse[0, rows], ref_lse[0, rows], "bf16", "prefill full")
     _say(f"prefill full normwise rel err {err:.2e} on {len(rows)} rows")
