@@ -54,10 +54,12 @@ struct PfLds {
   static constexpr int kTotal = 2 * kStage;
 };
 
-// Position of value column d inside a 16-key step of the V tile.  The XOR
-// of its low three bits with bits 3-5 keeps each group of 8 columns in place
-// (reads stay conflict-free) while the cooperative stores, whose lanes are 8
-// columns apart, spread over the LDS banks.
+// V tile in LDS: for 16-key step s, lane half h and value column d, the 16
+// bytes at slot (s * 2 + h) * d_v + vswz(d) hold that column's 8 keys of the
+// half, so the 32 lanes of a half read one contiguous run (no bank
+// conflicts).  vswz XORs a column's low three bits with bits 3-5: each group
+// of 8 columns stays in place for the reads while the cooperative stores,
+// whose lanes are 8 columns apart, spread over the banks.
 __device__ __forceinline__ int vswz(int d) { return d ^ ((d >> 3) & 7); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
@@ -135,22 +137,39 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   u32x4 kreg[KCH];
   u32x4 vreg[4];
 
-  // Rows past n_keys are clamped to the last visible row: the loads stay
-  // unconditional and in bounds, and every score they feed is masked.
+  // Per-thread base pointers of the cooperative loads; a tile adds j0 rows.
+  // Rows past n_keys (only in the last tile) are clamped to the last
+  // visible row: the loads stay in bounds and every score they feed is
+  // masked.
+  const bf16* kthr[KCH];
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) {
+    const int e = tid + c * 256;
+    kthr[c] = kbase + (size_t)(e / K16) * DK + (e % K16) * 8;
+  }
+  const bf16* vthr = vbase + (size_t)(v_kq * 4) * DV + v_dc * 8;
   auto load_tile = [&](int t) {
     const int j0 = t * kPfKeys;
+    if (j0 + kPfKeys <= n_keys) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int e = tid + c * 256;
-      const int key = e / K16, ch = e % K16;
-      const int j = min(j0 + key, n_keys - 1);
-      kreg[c] = load16(kbase + (size_t)j * DK + ch * 8);
-    }
-    if (v_act) {
+      for (int c = 0; c < KCH; ++c) kreg[c] = load16(kthr[c] + (size_t)j0 * DK);
+      if (v_act) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int j = min(j0 + v_kq * 4 + k, n_keys - 1);
-        vreg[k] = load16(vbase + (size_t)j * DV + v_dc * 8);
+        for (int k = 0; k < 4; ++k) vreg[k] = load16(vthr + (size_t)(j0 + k) * DV);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) {
+        const int e = tid + c * 256;
+        const int j = min(j0 + e / K16, n_keys - 1);
+        kreg[c] = load16(kbase + (size_t)j * DK + (e % K16) * 8);
+      }
+      if (v_act) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int j = min(j0 + v_kq * 4 + k, n_keys - 1);
+          vreg[k] = load16(vbase + (size_t)j * DV + v_dc * 8);
+        }
       }
     }
   };
@@ -179,8 +198,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         const uint32_t hi01 = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
         const uint32_t hi23 = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
         const int d0 = v_dc * 8 + 2 * dw;
-        uint2* p0 = reinterpret_cast<uint2*>(vl + ((s * DV + vswz(d0)) * 2 + hh) * 16 + off);
-        uint2* p1 = reinterpret_cast<uint2*>(vl + ((s * DV + vswz(d0 + 1)) * 2 + hh) * 16 + off);
+        uint2* p0 = reinterpret_cast<uint2*>(vl + ((s * 2 + hh) * DV + vswz(d0)) * 16 + off);
+        uint2* p1 = reinterpret_cast<uint2*>(vl + ((s * 2 + hh) * DV + vswz(d0 + 1)) * 16 + off);
         *p0 = make_uint2(lo01, lo23);
         *p1 = make_uint2(hi01, hi23);
       }
@@ -235,7 +254,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) smax = fmaxf(smax, fmaxf(s[kb][r], s[kb][r + 1]));
+      for (int r = 0; r < 16; r += 2) smax = fmaxf(fmaxf(smax, s[kb][r]), s[kb][r + 1]);
     }
     smax = fmaxf(smax, __shfl_xor(smax, 32));
     // Lazy rescaling: the running max only moves (and O, l are rescaled)
@@ -276,7 +295,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            vl + ((st * DV + vswz(n * 32 + col)) * 2 + h) * 16));
+            vl + ((st * 2 + h) * DV + vswz(n * 32 + col)) * 16));
         o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[n], 0, 0, 0);
       }
     }
@@ -388,8 +407,10 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
 
 template <int DK, int DV>
 static hipError_t launch_prefill_dd(const PrefillArgs& a) {
-  // An exact fp32 row sum whenever lse is returned (or merged across splits).
-  if (a.lse != nullptr || a.n_split > 1) return launch_prefill_t<DK, DV, true>(a);
+  // An exact fp32 row sum whenever lse is returned.  Without lse the split
+  // merge weights carry the rounded sums' ~2^-9 relative error, far below
+  // the bf16 output's own rounding.
+  if (a.lse != nullptr) return launch_prefill_t<DK, DV, true>(a);
   return launch_prefill_t<DK, DV, false>(a);
 }
 

@@ -384,6 +384,11 @@ def main():
         print(json.dumps({"copy_probe_bytes": a.numel() * 4, "copies": 3}))
         return
 
+    if args.workload.startswith("prefill"):
+        # Prefill alone (for profilers): the decode metric is not measured.
+        log(f"workload {args.workload}: prefill only")
+        print(json.dumps({"prefill": prefill_bench(args.steps)}), flush=True)
+        return
     log(f"workload {args.workload}: building inputs")
     bench = DecodeBench(args.workload, args.chunk)
     log(f"replicas {bench.replicas}, chunk {bench.S} rows, workspace {bench.ws_bytes} B")
