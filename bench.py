@@ -66,6 +66,12 @@ def parse():
     return p.parse_args()
 
 
+def kv_elements_per_token(n_k: int, d_k: int, n_v: int, d_v: int) -> int:
+    """Cache elements one token adds: n_k*d_k + n_v*d_v (the per-token factor
+    of the KV-cache cost model, Eq. (1) of the Pith review page)."""
+    return n_k * d_k + n_v * d_v
+
+
 TWINS = {"decode32k_asym": "decode32k_sym", "decode64k_dk64": "decode64k_sym",
          "decode64k_dk128": "decode64k_sym"}
 
@@ -119,7 +125,7 @@ class DecodeBench:
         self.k_new, self.v_new = up(k_new), up(v_new)
         self.pos = torch.from_numpy(pos.astype(np.int32)).to(dev)
         self.ctx_t = torch.from_numpy(ctx.astype(np.int32)).to(dev)
-        beta = (n_k * d_k + n_v * d_v) * esize
+        beta = kv_elements_per_token(n_k, d_k, n_v, d_v) * esize
         self.cache_bytes_attended = int(ctx.sum()) * beta
         self.alg_bytes_split = self.cache_bytes_attended + B * n_q * d_k * esize
         self.alg_bytes_step = (self.alg_bytes_split + B * n_q * d_v * esize
@@ -165,8 +171,14 @@ class DecodeBench:
         assert st == 0, st
 
     def step(self, r):
-        self.split(r)
-        self.combine()
+        """One decode step: append + attend + merge (diffqkv_decode_append)."""
+        k, v = self.caches[r]
+        st = self.lib.diffqkv_decode_append(
+            *self.shape, self.dtype_code, self.B, self.l_cap, self.max_ctx, self.case.scale,
+            self.q.data_ptr(), self.k_new.data_ptr(), self.v_new.data_ptr(), k.data_ptr(),
+            v.data_ptr(), self.ctx_t.data_ptr(), self.out.data_ptr(), self.lse.data_ptr(),
+            self.chunk, self.ws.data_ptr(), self.ws_bytes, self._stream())
+        assert st == 0, st
 
     # -- timing -------------------------------------------------------------
 
@@ -349,7 +361,7 @@ def cpu_baseline(name: str, seconds: float):
     q, k, v = case.widened()
     ctx = np.asarray(case.ctx_len)
     esize = 2 if case.dtype == "bf16" else 4
-    byts = int(ctx.sum()) * (case.n_k * case.d_k + case.n_v * case.d_v) * esize
+    byts = int(ctx.sum()) * kv_elements_per_token(case.n_k, case.d_k, case.n_v, case.d_v) * esize
     n = 0
     t0 = time.perf_counter()
     while True:
