@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   // thread owns 4 consecutive keys x 8 consecutive columns.
   const int v_dc = tid % VD8;            // column chunk
   const int v_kq = tid / VD8;            // key quad (0..15 when active)
-  const bool v_act = v_kq < kPfKeys / 4;
+  const bool v_act = VD8 * (kPfKeys / 4) >= 256 || v_kq < kPfKeys / 4;
   u32x4 kreg[KCH];
   u32x4 vreg[4];
 
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 
   for (int t = t_begin; t < t_end; ++t) {
     const int stage = (t - t_begin) & 1;
-    if (t + 1 < t_end) load_tile(t + 1);
+    load_tile(t + 1);  // past the last tile: clamped rows, stored but never read
     const unsigned char* kl = lds + stage * Lds::kStage;
     const unsigned char* vl = kl + Lds::kKBytes;
     const int j0 = t * kPfKeys;
@@ -273,8 +273,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     float psum = 0.f;
     const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
     bf16x8 pb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    // P for one 32-key block: exponentials, row sums, bf16 operands.
+    auto make_p = [&](int kb) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(fmaf(s[kb][r], qscale, -m_use));
@@ -285,22 +285,41 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         pb[kb * 2 + (r >> 3)][r & 7] = pk[0];
         pb[kb * 2 + (r >> 3)][(r & 7) + 1] = pk[1];
       }
-    }
-    psum += __shfl_xor(psum, 32);
-    l_run += psum;
-
-    // O^T += V^T P^T over four 16-key steps.
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    };
+    // O^T += V^T P^T for one 16-key step.
+    auto pv = [&](int st) {
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
             vl + ((st * 2 + h) * DV + vswz(n * 32 + col)) * 16));
         o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[n], 0, 0, 0);
       }
+    };
+    // Software overlap inside the tile: the matrix products of keys 0-31
+    // run while the VALU computes P for keys 32-63, and those of keys 32-63
+    // while it rearranges the next tile into LDS.
+    make_p(0);
+    pv(0);
+    pv(1);
+    make_p(1);
+#pragma unroll
+    for (int k = 0; k < 2 * NB; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
     }
-
-    if (t + 1 < t_end) store_tile(stage ^ 1);
+    psum += __shfl_xor(psum, 32);
+    l_run += psum;
+    pv(2);
+    pv(3);
+    store_tile(stage ^ 1);  // the last tile stores a clamped copy no one reads
+#pragma unroll
+    for (int k = 0; k < 2 * NB; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+    }
     __syncthreads();
   }
 
