@@ -37,8 +37,11 @@ int to_status(hipError_t e) { return e == hipSuccess ? DQKV_OK : DQKV_ERR_HIP; }
 
 // Rows per context chunk: enough (sequence, head-quad, chunk) workgroups to
 // give every CU about kWavesPerCUTarget waves, in multiples of 64 rows.
-int plan_chunk(int n_q, int batch, int max_ctx) {
-  const long long quads = (long long)batch * ((n_q + 3) / 4);
+int plan_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx) {
+  // Waves per (sequence, chunk): one per query head, or per pair of query
+  // heads that share their K and V heads (see the split kernel).
+  const int H = (n_q == 2 * n_v && (n_q / n_k) % 2 == 0) ? 2 : 1;
+  const long long quads = (long long)batch * ((n_q / H + 3) / 4);
   const long long want_wg = (long long)kCUs * kWavesPerCUTarget / 4;
   long long chunks_per_seq = (want_wg + quads - 1) / quads;
   if (chunks_per_seq < 1) chunks_per_seq = 1;
@@ -82,9 +85,10 @@ size_t workspace_bytes(int n_q, int d_v, int batch, int C) {
   return align256(parts * 2 * sizeof(float)) + parts * d_v * sizeof(float);
 }
 
-int resolve_chunk(int n_q, int batch, int max_ctx, int chunk_tokens, int* S) {
+int resolve_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx, int chunk_tokens,
+                  int* S) {
   if (chunk_tokens < 0 || chunk_tokens % kMinChunk != 0) return DQKV_ERR_SHAPE;
-  *S = chunk_tokens ? chunk_tokens : plan_chunk(n_q, batch, max_ctx);
+  *S = chunk_tokens ? chunk_tokens : plan_chunk(n_q, n_k, n_v, batch, max_ctx);
   if (chunks_for(max_ctx, *S) > kMaxChunks) return DQKV_ERR_UNSUPPORTED;
   return DQKV_OK;
 }
@@ -113,7 +117,7 @@ int32_t diffqkv_decode_chunk(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
   int st = check_heads(n_q, n_k, n_v, d_k, d_v);
   if (st) return st;
   if (batch < 0 || max_ctx < 0) return DQKV_ERR_SHAPE;
-  return resolve_chunk(n_q, batch, max_ctx, 0, chunk_tokens);
+  return resolve_chunk(n_q, n_k, n_v, batch, max_ctx, 0, chunk_tokens);
 }
 
 int32_t diffqkv_decode_workspace(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
@@ -124,7 +128,7 @@ int32_t diffqkv_decode_workspace(int32_t n_q, int32_t n_k, int32_t n_v, int32_t 
   if (st) return st;
   if (batch < 0 || max_ctx < 0) return DQKV_ERR_SHAPE;
   int S = 0;
-  st = resolve_chunk(n_q, batch, max_ctx, chunk_tokens, &S);
+  st = resolve_chunk(n_q, n_k, n_v, batch, max_ctx, chunk_tokens, &S);
   if (st) return st;
   *bytes = workspace_bytes(n_q, d_v, batch, chunks_for(max_ctx, S));
   return DQKV_OK;
@@ -176,7 +180,7 @@ static int prepare_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, in
       (need_out && !aligned16(out)) || !aligned16(workspace))
     return DQKV_ERR_ALIGN;
   int S = 0;
-  st = resolve_chunk(n_q, batch, max_ctx, chunk_tokens, &S);
+  st = resolve_chunk(n_q, n_k, n_v, batch, max_ctx, chunk_tokens, &S);
   if (st) return st;
   const int C = chunks_for(max_ctx, S);
   if ((long long)(n_q + 3) / 4 > 65535) return DQKV_ERR_UNSUPPORTED;

@@ -6,11 +6,12 @@
 //   s_j = scale * q_i . K[floor(i n_k / n_q)][j],     j < ctx_len[b]
 //   o_i = sum_j softmax(s)_j V[floor(i n_v / n_q)][j]
 //
-// Split kernel: one wavefront per (sequence, query head, context chunk); a
-// workgroup holds the four consecutive query heads of one chunk, so when
-// n_q / n_k >= 4 its four waves read the same K rows (the first wave to touch
-// a row brings it from HBM, the others hit the CU's L1 / the XCD's L2).  Each
-// wave walks its chunk in tiles of 64 rows:
+// Split kernel: one wavefront per (sequence, query head -- or pair of query
+// heads that share their K and V heads --, context chunk); a workgroup holds
+// four consecutive waves of one chunk, so when n_q / n_k >= 4 its waves read
+// the same K rows (the first wave to touch a row brings it from HBM, the
+// others hit the CU's L1 / the XCD's L2).  Each wave walks its chunk in tiles
+// of 64 rows:
 //   * all K and V loads of the tile are issued at once (16-byte lane loads,
 //     1 KiB contiguous per wave instruction);
 //   * scores: each lane multiplies its 16-byte slice of a K row with the
@@ -37,7 +38,10 @@ namespace dqkv {
 
 constexpr int kTile = 64;  // rows per wave iteration: one score per lane
 
-template <typename T, int DK, int DV>
+// H = query heads per wave.  With H = 2 the wave takes two consecutive query
+// heads that share one K head and one V head (n_q = 2 n_v): each K and V row
+// it loads serves both, halving the per-CU load traffic of such layouts.
+template <typename T, int DK, int DV, int H>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const T* __restrict__ q, const T* kc, const T* vc,
     const int32_t* __restrict__ ctx_len, float* __restrict__ part_ml,
@@ -59,22 +63,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
   const int c = blockIdx.x, quad = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = quad * 4 + wave;
-  if (i >= n_q) return;
+  const int i0 = (quad * 4 + wave) * H;   // this wave's first query head
+  if (i0 >= n_q) return;
   int L = ctx_len[b];
   L = max(0, min(L, min(max_ctx, l_cap)));
   const int j0 = c * S;
   if (j0 >= L) return;
   const int rows = min(S, L - j0);
-  const int hk = (i * n_k) / n_q;
-  const int hv = (i * n_v) / n_q;
+  const int hk = (i0 * n_k) / n_q;        // shared by the wave's H heads
+  const int hv = (i0 * n_v) / n_q;
 
-  // This lane's slice of q (scaled by scale * log2 e).
+  // This lane's slice of q for each head (scaled by scale * log2 e).
   const int kl = lane % LPR_K, kr = lane / LPR_K;
-  float qf[EPL];
-  Elem<T>::unpack(load16(q + ((size_t)b * n_q + i) * DK + kl * EPL), qf);
+  float qf[H][EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) qf[e] *= qscale;
+  for (int hh = 0; hh < H; ++hh) {
+    Elem<T>::unpack(load16(q + ((size_t)b * n_q + i0 + hh) * DK + kl * EPL), qf[hh]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[hh][e] *= qscale;
+  }
 
   const T* kp = kc + (((size_t)b * n_k + hk) * l_cap + j0) * DK + kl * EPL;
   const int vl = lane % LPR_V, vr = lane / LPR_V;
@@ -82,16 +89,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
   // Fused append: the sequence's newest row (L - 1) is read from k_new /
   // v_new instead of the cache, and written to the cache by one wave per
-  // K head and per V head.  Only this chunk touches row L - 1.
+  // K head (the one holding the group's first query head) and per V head.
+  // Only this chunk touches row L - 1.
   const bool fused = k_new != nullptr;
   const int r_new = fused ? L - 1 - j0 : -1;  // in [0, rows) iff this chunk owns it
   const T* kn = fused ? k_new + ((size_t)b * n_k + hk) * DK + kl * EPL : nullptr;
   const T* vn = fused ? v_new + ((size_t)b * n_v + hv) * DV + vl * EPL : nullptr;
   if (fused && r_new < rows) {
-    if (i % (n_q / n_k) == 0 && lane < LPR_K)
+    if (i0 % (n_q / n_k) == 0 && lane < LPR_K)
       *reinterpret_cast<u32x4*>(kc_w + (((size_t)b * n_k + hk) * l_cap + L - 1) * DK + kl * EPL) =
           load16(kn);
-    if (i % (n_q / n_v) == 0 && lane < LPR_V)
+    if (i0 % (n_q / n_v) == 0 && lane < LPR_V)
       *reinterpret_cast<u32x4*>(vc_w + (((size_t)b * n_v + hv) * l_cap + L - 1) * DV + vl * EPL) =
           load16(vn);
   }
@@ -101,10 +109,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   // (r % RPL_K) * LPR_K + r / RPL_K.
   const int my_row = kl * RPL_K + kr;
 
-  float m_run = -INFINITY, l_run = 0.f;
-  float acc[EPL];
+  float m_run[H], l_run[H], acc[H][EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int hh = 0; hh < H; ++hh) {
+    m_run[hh] = -INFINITY;
+    l_run[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
+  }
 
   auto load_k = [&](int r) -> u32x4 {
     if (r >= rows) return u32x4{0u, 0u, 0u, 0u};
@@ -114,41 +126,49 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     if (r >= rows) return u32x4{0u, 0u, 0u, 0u};
     return r == r_new ? load16(vn) : load16_nt(vp + (size_t)r * DV);
   };
-  // Scores of the tile at t0 from its K loads; online-softmax update.
-  // Returns this lane's probability (of row my_row).
-  auto scores = [&](int t0, const u32x4 (&kv)[NK]) -> float {
-    float s_mine = 0.f;
-#pragma unroll
-    for (int u = 0; u < NK; ++u) {
-      float kf[EPL];
-      Elem<T>::unpack(kv[u], kf);
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s = fmaf(qf[e], kf[e], s);
-      s = group_sum<LPR_K>(s);
-      s_mine = (u == kl) ? s : s_mine;
-    }
-    if (t0 + my_row >= rows) s_mine = -INFINITY;
-    const float m_new = fmaxf(m_run, wave_max(s_mine));
-    const float p = fast_exp2(s_mine - m_new);
-    const float alpha = fast_exp2(m_run - m_new);
-    l_run = l_run * alpha + wave_sum(p);
-    m_run = m_new;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
-    return p;
-  };
 
   // One tile of 64 rows per iteration: all of its K loads and the first VB
-  // V loads are issued together, the scores wait only for K.  (Holding a
-  // second tile in registers costs occupancy and measured slower.)
+  // V loads are issued together and the scores wait only for K.  (Keeping a
+  // second tile's loads in flight -- double buffers, or re-filling each
+  // register right after use -- costs occupancy and measured slower.)
   for (int t0 = 0; t0 < rows; t0 += kTile) {
     u32x4 kv[NK], vv[VB];
 #pragma unroll
     for (int u = 0; u < NK; ++u) kv[u] = load_k(t0 + u * RPL_K + kr);
 #pragma unroll
     for (int u = 0; u < VB; ++u) vv[u] = load_v(t0 + u * RPL_V + vr);
-    const float p = scores(t0, kv);
+
+    // Scores (one row per lane per head) and the online-softmax update.
+    float s_mine[H];
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh) s_mine[hh] = 0.f;
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      float kf[EPL];
+      Elem<T>::unpack(kv[u], kf);
+#pragma unroll
+      for (int hh = 0; hh < H; ++hh) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s = fmaf(qf[hh][e], kf[e], s);
+        s = group_sum<LPR_K>(s);
+        s_mine[hh] = (u == kl) ? s : s_mine[hh];
+      }
+    }
+    float p[H];
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh) {
+      if (t0 + my_row >= rows) s_mine[hh] = -INFINITY;
+      const float m_new = fmaxf(m_run[hh], wave_max(s_mine[hh]));
+      p[hh] = fast_exp2(s_mine[hh] - m_new);
+      const float alpha = fast_exp2(m_run[hh] - m_new);
+      l_run[hh] = l_run[hh] * alpha + wave_sum(p[hh]);
+      m_run[hh] = m_new;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
+    }
+
+    // acc_h += p_h(row) * V_row for every head of the wave.
 #pragma unroll
     for (int vb = 0; vb < NV; vb += VB) {
       if (vb > 0) {  // only for fp32 with wide V rows: next batch of loads
@@ -158,30 +178,39 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
         const int r = (vb + u) * RPL_V + vr;  // row within the tile
-        const float pr = __shfl(p, (r % RPL_K) * LPR_K + r / RPL_K);
+        const int src = (r % RPL_K) * LPR_K + r / RPL_K;
         float vf[EPL];
         Elem<T>::unpack(vv[u], vf);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pr, vf[e], acc[e]);
+        for (int hh = 0; hh < H; ++hh) {
+          const float pr = __shfl(p[hh], src);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pr, vf[e], acc[hh][e]);
+        }
       }
     }
   }
 
-  // Sum the row groups of the wave (lanes with equal vl).
+  // Sum the row groups of the wave (lanes with equal vl) and write each
+  // head's partial.
 #pragma unroll
-  for (int off = LPR_V; off < 64; off <<= 1) {
+  for (int hh = 0; hh < H; ++hh) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], off);
-  }
-  const size_t pidx = ((size_t)b * n_q + i) * C + c;
-  if (vr == 0) {
-    f32x4* dst = reinterpret_cast<f32x4*>(part_acc + pidx * DV + vl * EPL);
+    for (int off = LPR_V; off < 64; off <<= 1) {
 #pragma unroll
-    for (int e = 0; e < EPL; e += 4) dst[e / 4] = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
-  }
-  if (lane == 0) {
-    part_ml[2 * pidx] = m_run;
-    part_ml[2 * pidx + 1] = l_run;
+      for (int e = 0; e < EPL; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], off);
+    }
+    const size_t pidx = ((size_t)b * n_q + i0 + hh) * C + c;
+    if (vr == 0) {
+      f32x4* dst = reinterpret_cast<f32x4*>(part_acc + pidx * DV + vl * EPL);
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4)
+        dst[e / 4] = f32x4{acc[hh][e], acc[hh][e + 1], acc[hh][e + 2], acc[hh][e + 3]};
+    }
+    if (lane == 0) {
+      part_ml[2 * pidx] = m_run[hh];
+      part_ml[2 * pidx + 1] = l_run[hh];
+    }
   }
 }
 
@@ -263,15 +292,30 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
 
 // ------------------------------------------------------------------ launch
 
+// Query heads per wave: two when consecutive pairs of query heads share both
+// their K head and their V head (n_q = 2 n_v and n_q / n_k even).
+static int heads_per_wave(const DecodeArgs& a) {
+  return (a.n_q == 2 * a.n_v && (a.n_q / a.n_k) % 2 == 0) ? 2 : 1;
+}
+
 template <typename T, int DK, int DV>
 static hipError_t launch_split_t(const DecodeArgs& a) {
   const float qscale = a.scale * kLog2e;
-  dim3 grid(a.C, (a.n_q + 3) / 4, a.batch);
-  hipLaunchKernelGGL((decode_split_kernel<T, DK, DV>), grid, dim3(256), 0, a.stream,
-                     (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.ctx_len,
-                     a.part_ml, a.part_acc, a.n_q, a.n_k, a.n_v, a.l_cap, a.max_ctx, a.S,
-                     a.C, qscale, (const T*)a.k_new, (const T*)a.v_new, (T*)a.k_cache,
-                     (T*)a.v_cache);
+  const int H = heads_per_wave(a);
+  dim3 grid(a.C, (a.n_q + 4 * H - 1) / (4 * H), a.batch);
+  if (H == 2) {
+    hipLaunchKernelGGL((decode_split_kernel<T, DK, DV, 2>), grid, dim3(256), 0, a.stream,
+                       (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.ctx_len,
+                       a.part_ml, a.part_acc, a.n_q, a.n_k, a.n_v, a.l_cap, a.max_ctx, a.S,
+                       a.C, qscale, (const T*)a.k_new, (const T*)a.v_new, (T*)a.k_cache,
+                       (T*)a.v_cache);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<T, DK, DV, 1>), grid, dim3(256), 0, a.stream,
+                       (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.ctx_len,
+                       a.part_ml, a.part_acc, a.n_q, a.n_k, a.n_v, a.l_cap, a.max_ctx, a.S,
+                       a.C, qscale, (const T*)a.k_new, (const T*)a.v_new, (T*)a.k_cache,
+                       (T*)a.v_cache);
+  }
   return hipGetLastError();
 }
 

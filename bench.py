@@ -60,6 +60,9 @@ def parse():
     p.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     p.add_argument("--kernel-only", action="store_true",
                    help="only run steps (for profilers); skip twin, prefill, CPU baseline")
+    p.add_argument("--ket", action="store_true",
+                   help="only run the kernel-execution-time comparison of the pages' SIGMA-1.5B "
+                        "and standard GQA attention shapes at prefixes 2k-32k and exit")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES bytes three times (calibrates "
                         "the HBM byte counters of a profiler) and exit")
@@ -288,6 +291,32 @@ def pmc_traffic(workload: str):
         return None
 
 
+def ket_replica(steps: int):
+    """Split- and combine-kernel times (each timed alone, graph replay) and
+    their sum, for SIGMA-1.5B vs the standard GQA shape, with the relative
+    improvement (STD - SIGMA) / STD the pages report per prefix length."""
+    import synth
+    rows = []
+    for prefix in synth.KET_PREFIXES:
+        t = {}
+        for model in ("sigma", "std"):
+            bn = DecodeBench(f"ket_{model}_{prefix}")
+            split_ms, comb_ms = bn.time_kernels(steps)
+            t[model] = (split_ms * 1e3, comb_ms * 1e3)
+            bn.free()
+            del bn
+        rel = [(t["std"][k] - t["sigma"][k]) / t["std"][k] for k in (0, 1)]
+        tot_s, tot_g = sum(t["sigma"]), sum(t["std"])
+        rows.append({"prefix": prefix,
+                     "sigma_us": {"split": round(t["sigma"][0], 2), "combine": round(t["sigma"][1], 2)},
+                     "std_us": {"split": round(t["std"][0], 2), "combine": round(t["std"][1], 2)},
+                     "improvement_pct": {"split": round(100 * rel[0], 2),
+                                         "combine": round(100 * rel[1], 2),
+                                         "total": round(100 * (tot_g - tot_s) / tot_g, 2)}})
+        log(json.dumps(rows[-1]))
+    return rows
+
+
 def prefill_bench(steps: int = 10):
     import numpy as np
     import torch
@@ -396,6 +425,11 @@ def main():
         print(json.dumps({"copy_probe_bytes": a.numel() * 4, "copies": 3}))
         return
 
+    if args.ket:
+        print(json.dumps({"ket_replica": ket_replica(args.steps),
+                          "note": "batch 1, one query token, bf16; kernel times from graphs "
+                                  "of back-to-back launches over cache replicas"}), flush=True)
+        return
     if args.workload.startswith("prefill"):
         # Prefill alone (for profilers): the decode metric is not measured.
         log(f"workload {args.workload}: prefill only")

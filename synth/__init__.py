@@ -208,12 +208,23 @@ def workload(name: str) -> dict:
         return dict(seed=4, dtype="bf16", batch=4, n_q=16, n_k=n_k, n_v=n_v,
                     d_k=d_k, d_v=d_v, ctx_len=65536, outlier_frac=0.01,
                     outlier_factor=8.0)
+    if name.startswith("ket_"):
+        # The pages' efficiency comparison: SIGMA-1.5B attention (32 query,
+        # 4 key, 16 value heads, head dimension 64) against their standard
+        # GQA model (16 key and 16 value heads), one sequence, at a prefix.
+        _, model, prefix = name.split("_")
+        n_k = {"sigma": 4, "std": 16}[model]
+        return dict(seed=6, dtype="bf16", batch=1, n_q=32, n_k=n_k, n_v=16, d_k=64,
+                    d_v=64, ctx_len=int(prefix))
     if name == "prefill2k_on_30k":
         return dict(seed=5, dtype="bf16", batch=1, n_q=16, n_k=4, n_v=16,
                     d_k=64, d_v=128, ctx_len=32768, t_new=2048)
     raise KeyError(name)
 
 
+KET_PREFIXES = (2048, 4096, 16384, 32768)
+
 WORKLOADS = ("tiny_f32", "decode32k_asym", "decode32k_sym", "ragged16",
              "decode64k_dk64", "decode64k_dk128", "decode64k_sym",
-             "prefill2k_on_30k")
+             "prefill2k_on_30k") + tuple(
+                 f"ket_{m}_{p}" for p in KET_PREFIXES for m in ("sigma", "std"))

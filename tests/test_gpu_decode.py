@@ -58,12 +58,16 @@ SMALL = [
     ("f32", 6, 3, 2, 64, 64, [130, 129, 1], 140),
     ("f32", 4, 2, 4, 32, 256, [200], 200),
     ("bf16", 16, 4, 16, 64, 128, [5000, 1, 64, 65, 129], 5000),
-    ("bf16", 32, 4, 16, 64, 64, [3000, 700], 3072),
+    ("bf16", 32, 4, 16, 64, 64, [3000, 700], 3072),     # SIGMA-1.5B heads
+    ("bf16", 32, 16, 16, 64, 64, [2100, 64], 2112),     # the pages' standard GQA
     ("bf16", 16, 16, 16, 128, 128, [2000], 2048),
     ("bf16", 16, 1, 16, 256, 256, [500], 512),
     ("bf16", 8, 8, 2, 32, 256, [777], 800),
     ("bf16", 16, 4, 16, 128, 128, [1500, 333], 1536),
     ("bf16", 12, 4, 12, 64, 128, [999], 1000),
+    ("bf16", 8, 4, 4, 64, 64, [1000, 3], 1024),          # head pairs share K and V
+    ("bf16", 12, 2, 6, 64, 128, [700], 704),            # pairs, last workgroup half full
+    ("f32", 8, 2, 4, 64, 64, [300], 320),
 ]
 
 
