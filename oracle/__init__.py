@@ -4,8 +4,10 @@ Imported by the test-suite, the smoke check and the benchmark's CPU-baseline
 leg; never by the GPU library.
 """
 
-from .attention import (attend_one, attention_weights, decode, default_scale,
-                        group_sharing_index, kv_append, prefill)
+from .attention import (attend_one, attend_selective_one, attention_weights, decode,
+                        decode_selective, default_scale, group_sharing_index, kv_append,
+                        prefill, top_k_rows)
 
-__all__ = ["attend_one", "attention_weights", "decode", "default_scale",
-           "group_sharing_index", "kv_append", "prefill"]
+__all__ = ["attend_one", "attend_selective_one", "attention_weights", "decode",
+           "decode_selective", "default_scale", "group_sharing_index", "kv_append",
+           "prefill", "top_k_rows"]

@@ -25,12 +25,18 @@ Readings taken where the pages are silent (all listed in the design doc):
   L rows attends keys 0 .. L - t_new + r       (not on the pages)
 * an empty context yields o = 0, lse = -inf    (never arises in a decoder)
 
+Selective-V decode (architecture page, "Selective V Cache Fetching") keeps
+the full softmax weights and sums only the V rows of the k largest; ties go
+to the lower row index (a reading: the page does not say).
+
 Pins (tests/test_oracle.py): the FlexHeadFA index worked example, reduction
 to textbook MHA / GQA / MQA (torch's scaled_dot_product_attention in fp64),
 weights summing to 1, brute-force softmax without max-shift on tiny shapes,
 the kv_group_sharing equivalence, closed forms (one key, zero scale, two keys
 with chosen logits), key-permutation invariance, prefill/decode consistency
-and causal masking, and Step 2's concatenation for the append.
+and causal masking, Step 2's concatenation for the append, and for
+selective V: k >= L equals full decode, k = 1 is the arg-max row times its
+weight, brute force on tiny shapes, and ties resolved to lower indices.
 """
 
 from __future__ import annotations
@@ -160,3 +166,52 @@ def kv_append(k_cache, v_cache, k_new, v_new, pos):
             k[b, :, row, :] = k_new[b, t]
             v[b, :, row, :] = v_new[b, t]
     return k, v
+
+
+def top_k_rows(alpha: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest weights, ties to the lower index, ascending.
+
+    Reading of the architecture page's TopK (section "Selective V Cache
+    Fetching"), which leaves ties open: the lower row index wins.
+    """
+    order = np.argsort(-np.asarray(alpha, dtype=np.float64), kind="stable")
+    return np.sort(order[:min(int(k), alpha.shape[0])])
+
+
+def attend_selective_one(q_i, K_i, V_i, scale: float, k: int, rows=None):
+    """o ~= sum over TopK(alpha) of alpha_j V_j, for one query head.
+
+    Architecture page, "Selective V Cache Fetching": alpha is the full
+    softmax over every visible row (the whole K cache is read); only the V
+    rows of the k largest weights are fetched and the others count as zero,
+    without renormalising.  ``rows`` overrides the selected set (to evaluate
+    the formula on a given set).  Returns ``(o, selected_rows)``.
+    """
+    if K_i.shape[0] == 0:
+        return np.zeros(V_i.shape[1], dtype=np.float64), np.zeros(0, dtype=np.int64)
+    alpha, _ = attention_weights(q_i, K_i, scale)
+    sel = top_k_rows(alpha, k) if rows is None else np.asarray(rows, dtype=np.int64)
+    return alpha[sel] @ np.asarray(V_i[sel], dtype=np.float64), sel
+
+
+def decode_selective(q, k_cache, v_cache, ctx_len, top_k: int, scale: float | None = None):
+    """Selective-V decode: per sequence and query head, the weighted sum of
+    the V rows with the top_k largest attention weights (architecture page,
+    "Selective V Cache Fetching"; head maps and scale as in :func:`decode`).
+    Returns ``(out[B][n_q][d_v], selected)`` with ``selected[b][i]`` the
+    ascending row indices."""
+    B, n_q, d_k = q.shape
+    n_k = k_cache.shape[1]
+    n_v, d_v = v_cache.shape[1], v_cache.shape[3]
+    if scale is None:
+        scale = default_scale(d_k)
+    out = np.zeros((B, n_q, d_v), dtype=np.float64)
+    selected = [[None] * n_q for _ in range(B)]
+    for b in range(B):
+        L = int(ctx_len[b])
+        for i in range(n_q):
+            g = group_sharing_index(i, n_q, n_k)
+            hv = group_sharing_index(i, n_q, n_v)
+            out[b, i], selected[b][i] = attend_selective_one(
+                q[b, i], k_cache[b, g, :L], v_cache[b, hv, :L], scale, top_k)
+    return out, selected

@@ -325,3 +325,52 @@ def test_pins_catch_planted_mistakes(monkeypatch):
                     break
             assert caught, f"no pin caught the planted mistake: {name}"
     assert A.group_sharing_index is real_gsi
+
+
+# ------------------------------------------------------------- selective V
+
+def test_selective_with_k_at_least_length_is_full_decode():
+    q, k, v, lens = _case(31, 2, 8, 2, 4, 16, 32, 50)
+    full, _ = oracle.decode(q, k, v, lens)
+    for top_k in (50, 51, 1000):
+        sel, rows = oracle.decode_selective(q, k, v, lens, top_k)
+        np.testing.assert_allclose(sel, full, rtol=1e-13, atol=1e-15)
+        assert all(len(r) == 50 for rb in rows for r in rb)
+
+
+def test_selective_top1_is_the_argmax_row():
+    q, k, v, lens = _case(32, 1, 4, 1, 4, 16, 8, 40)
+    sel, rows = oracle.decode_selective(q, k, v, lens, 1)
+    scale = 1 / math.sqrt(16)
+    for i in range(4):
+        s = scale * (k[0, 0, :40] @ q[0, i])
+        j = int(np.argmax(s))
+        alpha_j = math.exp(s[j]) / np.exp(s).sum()
+        assert list(rows[0][i]) == [j]
+        np.testing.assert_allclose(sel[0, i], alpha_j * v[0, i, j], rtol=1e-13)
+
+
+def test_selective_brute_force_tiny():
+    n_q, n_k, n_v, d_k, d_v, L, top_k = 4, 2, 2, 3, 5, 9, 4
+    q, k, v, lens = _case(33, 1, n_q, n_k, n_v, d_k, d_v, L)
+    sel, _ = oracle.decode_selective(q, k, v, lens, top_k)
+    scale = 1.0 / math.sqrt(d_k)
+    for i in range(n_q):
+        kh, vh = i * n_k // n_q, i * n_v // n_q
+        s = [scale * sum(q[0, i, d] * k[0, kh, j, d] for d in range(d_k)) for j in range(L)]
+        z = sum(math.exp(x) for x in s)
+        a = [math.exp(x) / z for x in s]
+        best = sorted(range(L), key=lambda j: (-a[j], j))[:top_k]
+        for d in range(d_v):
+            assert abs(sel[0, i, d] - sum(a[j] * v[0, vh, j, d] for j in best)) < 1e-12
+
+
+def test_selective_ties_go_to_lower_rows():
+    # All keys equal: every weight is 1/L; the first k rows are selected.
+    q = _rand(34, 1, 2, 8)
+    k = np.repeat(_rand(35, 1, 1, 1, 8), 30, axis=2)
+    v = _rand(36, 1, 2, 30, 4)
+    sel, rows = oracle.decode_selective(q, k, v, np.array([30]), 7)
+    for i in range(2):
+        assert list(rows[0][i]) == list(range(7))
+        np.testing.assert_allclose(sel[0, i], v[0, i, :7].sum(axis=0) / 30, rtol=1e-13)
