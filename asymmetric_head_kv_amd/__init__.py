@@ -21,8 +21,8 @@ import os
 import torch
 
 __all__ = ["DQKVError", "lib_path", "load", "decode", "decode_chunk",
-           "decode_workspace_bytes", "prefill", "prefill_workspace_bytes", "kv_append",
-           "STATUS"]
+           "decode_workspace_bytes", "decode_selective", "selective_workspace_bytes",
+           "prefill", "prefill_workspace_bytes", "kv_append", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libdiffqkv.so")
@@ -46,6 +46,8 @@ SIGNATURES = {
     "diffqkv_decode_split": (_i32, [_i32] * 9 + [_f32] + [_vp] * 6 + [_i32, _vp, _sz, _vp]),
     "diffqkv_decode_append": (_i32, [_i32] * 9 + [_f32] + [_vp] * 8 + [_i32, _vp, _sz, _vp]),
     "diffqkv_decode_combine": (_i32, [_i32] * 9 + [_vp] * 3 + [_i32, _vp, _sz, _vp]),
+    "diffqkv_decode_selective_workspace": (_i32, [_i32] * 8 + [ctypes.POINTER(_sz)]),
+    "diffqkv_decode_selective": (_i32, [_i32] * 9 + [_f32, _i32] + [_vp] * 10 + [_sz, _vp]),
 }
 
 _lib = None
@@ -199,6 +201,59 @@ def decode(q, k_cache, v_cache, ctx_len, *, max_ctx=None, scale=None, out=None,
             _ptr(out), _ptr(lse), int(chunk_tokens), _ptr(workspace), ws_bytes,
             _stream(stream)))
     return out, lse
+
+
+def selective_workspace_bytes(n_q, n_k, n_v, d_k, d_v, batch, max_ctx, top_k) -> int:
+    out = _sz()
+    _check("diffqkv_decode_selective_workspace",
+           load().diffqkv_decode_selective_workspace(n_q, n_k, n_v, d_k, d_v, batch, max_ctx,
+                                                     top_k, ctypes.byref(out)))
+    return out.value
+
+
+def decode_selective(q, k_cache, v_cache, ctx_len, *, top_k=100, max_ctx=None, scale=None,
+                     out=None, lse=None, sel_idx=None, workspace=None, k_new=None,
+                     v_new=None, stream=None):
+    """Decode with selective V fetching: only the V rows of each query
+    head's top_k attention weights are read and summed with their (full
+    softmax) weights.  Returns (out [B, n_q, d_v], lse or None, sel_idx or
+    None); pass sel_idx (int32 [B, n_q, top_k]) to receive the chosen rows.
+    k_new / v_new fuse the append of the step's token as in decode()."""
+    _device_tensors(q, k_cache, v_cache, ctx_len, out, lse, sel_idx, workspace, k_new, v_new)
+    B, n_q, d_k = q.shape
+    n_k, l_cap = k_cache.shape[1], k_cache.shape[2]
+    n_v, d_v = v_cache.shape[1], v_cache.shape[3]
+    if k_cache.shape != (B, n_k, l_cap, d_k) or v_cache.shape[:3] != (B, n_v, l_cap):
+        raise ValueError("inconsistent q / cache shapes")
+    if ctx_len.dtype != torch.int32 or ctx_len.numel() != B:
+        raise ValueError("ctx_len must be int32 [B]")
+    for t in (k_cache, v_cache, k_new, v_new):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError("q, the caches and the new rows must share one dtype")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None and (k_new.numel() != B * n_k * d_k or v_new.numel() != B * n_v * d_v):
+        raise ValueError("k_new must hold [B, n_k, d_k] and v_new [B, n_v, d_v]")
+    max_ctx = l_cap if max_ctx is None else int(max_ctx)
+    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    top_k = int(top_k)
+    if out is None:
+        out = torch.empty((B, n_q, d_v), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, n_q, d_v) or out.dtype != q.dtype:
+        raise ValueError("out must be [B, n_q, d_v] in q's dtype")
+    if lse is not None and (lse.shape != (B, n_q) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, n_q]")
+    if sel_idx is not None and (sel_idx.shape != (B, n_q, top_k) or sel_idx.dtype != torch.int32):
+        raise ValueError("sel_idx must be int32 [B, n_q, top_k]")
+    if workspace is None:
+        need = selective_workspace_bytes(n_q, n_k, n_v, d_k, d_v, B, max_ctx, top_k)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("diffqkv_decode_selective", load().diffqkv_decode_selective(
+        n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, l_cap, max_ctx, scale, top_k,
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
+        _ptr(out), _ptr(lse), _ptr(sel_idx), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse, sel_idx
 
 
 def prefill_workspace_bytes(n_q, n_k, n_v, d_k, d_v, batch, t_new) -> int:

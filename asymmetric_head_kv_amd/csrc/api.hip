@@ -37,11 +37,10 @@ int to_status(hipError_t e) { return e == hipSuccess ? DQKV_OK : DQKV_ERR_HIP; }
 
 // Rows per context chunk: enough (sequence, head-quad, chunk) workgroups to
 // give every CU about kWavesPerCUTarget waves, in multiples of 64 rows.
-int plan_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx) {
-  // Waves per (sequence, chunk): one per query head, or per pair of query
-  // heads that share their K and V heads (see the split kernel).
-  const int H = (n_q == 2 * n_v && (n_q / n_k) % 2 == 0) ? 2 : 1;
-  const long long quads = (long long)batch * ((n_q / H + 3) / 4);
+// H = query heads per wave.
+int plan_chunk_h(int n_q, int H, int batch, int max_ctx) {
+  long long quads = (long long)batch * ((n_q / H + 3) / 4);
+  if (quads < 1) quads = 1;  // an empty batch launches nothing
   const long long want_wg = (long long)kCUs * kWavesPerCUTarget / 4;
   long long chunks_per_seq = (want_wg + quads - 1) / quads;
   if (chunks_per_seq < 1) chunks_per_seq = 1;
@@ -52,6 +51,13 @@ int plan_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx) {
   if (S < s_floor) S = (s_floor + kMinChunk - 1) / kMinChunk * kMinChunk;
   if (S > (1 << 30)) S = 1 << 30;
   return (int)S;
+}
+
+int plan_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx) {
+  // Waves per (sequence, chunk): one per query head, or per pair of query
+  // heads that share their K and V heads (see the split kernel).
+  const int H = (n_q == 2 * n_v && (n_q / n_k) % 2 == 0) ? 2 : 1;
+  return plan_chunk_h(n_q, H, batch, max_ctx);
 }
 
 int chunks_for(int max_ctx, int S) {
@@ -90,6 +96,32 @@ int resolve_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx, int chunk_t
   if (chunk_tokens < 0 || chunk_tokens % kMinChunk != 0) return DQKV_ERR_SHAPE;
   *S = chunk_tokens ? chunk_tokens : plan_chunk(n_q, n_k, n_v, batch, max_ctx);
   if (chunks_for(max_ctx, *S) > kMaxChunks) return DQKV_ERR_UNSUPPORTED;
+  return DQKV_OK;
+}
+
+// Workspace of a selective-V decode: logits, per-range (max, sum), and the
+// per-range candidates (logit, row).
+struct SelLayout {
+  int S, C, ld_s, n_ranges;
+  size_t off_ml, off_cs, off_ci, total;
+};
+
+int selective_layout(int n_q, int batch, int max_ctx, int top_k, SelLayout* o) {
+  if (top_k < 1) return DQKV_ERR_SHAPE;
+  if (top_k > dqkv::kMaxTopK) return DQKV_ERR_UNSUPPORTED;
+  o->S = plan_chunk_h(n_q, 1, batch, max_ctx);
+  o->C = chunks_for(max_ctx, o->S);
+  if (o->C > kMaxChunks) return DQKV_ERR_UNSUPPORTED;
+  o->ld_s = (int)(((long long)max_ctx + 63) / 64 * 64);
+  if (o->ld_s < 64) o->ld_s = 64;
+  o->n_ranges = (int)(((long long)max_ctx + dqkv::kSelRows - 1) / dqkv::kSelRows);
+  if (o->n_ranges < 1) o->n_ranges = 1;
+  const size_t heads = (size_t)batch * n_q;
+  o->off_ml = align256(heads * o->ld_s * sizeof(float));
+  o->off_cs = o->off_ml + align256(heads * o->n_ranges * 2 * sizeof(float));
+  const size_t cand = heads * o->n_ranges * (size_t)top_k;
+  o->off_ci = o->off_cs + align256(cand * sizeof(float));
+  o->total = o->off_ci + cand * sizeof(int32_t);
   return DQKV_OK;
 }
 
@@ -330,6 +362,63 @@ int32_t diffqkv_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int3
                      : nullptr;
   a.stream = (hipStream_t)stream;
   return to_status(dqkv::launch_prefill(a));
+}
+
+int32_t diffqkv_decode_selective_workspace(int32_t n_q, int32_t n_k, int32_t n_v,
+                                           int32_t d_k, int32_t d_v, int32_t batch,
+                                           int32_t max_ctx, int32_t top_k, size_t* bytes) {
+  if (!bytes) return DQKV_ERR_NULL;
+  int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+  if (st) return st;
+  if (batch < 0 || max_ctx < 0) return DQKV_ERR_SHAPE;
+  SelLayout lay;
+  st = selective_layout(n_q, batch, max_ctx, top_k, &lay);
+  if (st) return st;
+  *bytes = lay.total;
+  return DQKV_OK;
+}
+
+int32_t diffqkv_decode_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                                 int32_t d_v, int32_t dtype, int32_t batch, int32_t l_cap,
+                                 int32_t max_ctx, float scale, int32_t top_k, const void* q,
+                                 const void* k_new, const void* v_new, void* k_cache,
+                                 void* v_cache, const int32_t* ctx_len, void* out, float* lse,
+                                 int32_t* sel_idx, void* workspace,
+                                 size_t workspace_bytes_given, void* stream) {
+  int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+  if (st) return st;
+  st = check_dtype_dims(dtype, d_k, d_v);
+  if (st) return st;
+  if (batch < 0 || l_cap < 0 || max_ctx < 0 || max_ctx > l_cap || batch > 65535 ||
+      n_q > 65535)
+    return DQKV_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return DQKV_ERR_SHAPE;
+  SelLayout lay;
+  st = selective_layout(n_q, batch, max_ctx, top_k, &lay);
+  if (st) return st;
+  if (batch == 0) return DQKV_OK;
+  if ((k_new == nullptr) != (v_new == nullptr)) return DQKV_ERR_NULL;
+  if (!q || !k_cache || !v_cache || !ctx_len || !out || !workspace) return DQKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(workspace) || (k_new && (!aligned16(k_new) || !aligned16(v_new))))
+    return DQKV_ERR_ALIGN;
+  if (workspace_bytes_given < lay.total) return DQKV_ERR_WORKSPACE;
+  dqkv::SelectiveArgs a;
+  a.bf16 = dtype == DQKV_BF16;
+  a.n_q = n_q; a.n_k = n_k; a.n_v = n_v; a.d_k = d_k; a.d_v = d_v;
+  a.batch = batch; a.l_cap = l_cap; a.max_ctx = max_ctx;
+  a.S = lay.S; a.C = lay.C; a.ld_s = lay.ld_s; a.n_ranges = lay.n_ranges;
+  a.top_k = top_k; a.scale = scale;
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.ctx_len = ctx_len;
+  a.out = out; a.lse = lse; a.sel_idx = sel_idx;
+  char* ws = (char*)workspace;
+  a.scores = (float*)ws;
+  a.range_ml = (float*)(ws + lay.off_ml);
+  a.cand_s = (float*)(ws + lay.off_cs);
+  a.cand_i = (int32_t*)(ws + lay.off_ci);
+  a.k_new = k_new; a.v_new = v_new;
+  a.stream = (hipStream_t)stream;
+  return to_status(dqkv::launch_decode_selective(a));
 }
 
 }  // extern "C"

@@ -55,9 +55,39 @@ struct PrefillArgs {
   hipStream_t stream;
 };
 
+// Selective-V decode: rows per local-selection range, and the largest top_k.
+constexpr int kSelRows = 4096;
+constexpr int kMaxTopK = 1024;
+
+struct SelectiveArgs {
+  bool bf16;
+  int n_q, n_k, n_v, d_k, d_v;
+  int batch, l_cap, max_ctx;
+  int S, C;       // score-kernel chunk rows, chunks per sequence
+  int ld_s;       // row stride of the logit buffer (max_ctx rounded up to 64)
+  int n_ranges;   // ceil(max_ctx / kSelRows)
+  int top_k;
+  float scale;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* ctx_len;
+  void* out;
+  float* lse;
+  int32_t* sel_idx;   // [B][n_q][top_k] or null
+  float* scores;      // [B][n_q][ld_s]      base-2 logits
+  float* range_ml;    // [B][n_q][n_ranges][2]
+  float* cand_s;      // [B][n_q][n_ranges][top_k]
+  int32_t* cand_i;    // [B][n_q][n_ranges][top_k]
+  const void* k_new;  // fused append, or null
+  const void* v_new;
+  hipStream_t stream;
+};
+
 hipError_t launch_decode_split(const DecodeArgs& a);
 hipError_t launch_decode_combine(const DecodeArgs& a);
 hipError_t launch_kv_append(const AppendArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
+hipError_t launch_decode_selective(const SelectiveArgs& a);
 
 }  // namespace dqkv

@@ -1,0 +1,466 @@
+// Selective V fetching for decode (Sigma architecture page, section
+// "Selective V Cache Fetching"): the attention weights alpha_i of every query
+// head are computed over the whole K cache, but only the V rows of the top_k
+// largest weights are read, and the output is their alpha-weighted sum
+//   o_i ~= sum_{j in TopK(alpha_i)} alpha_ij V[floor(i n_v / n_q)][j]
+// with alpha the full softmax (no renormalisation over the selected rows).
+// Equal weights are ordered by row index, lower first.
+//
+// Three kernels, each one pass:
+//   1. score:  s_ij = (scale log2 e) q_i . K_j for every visible row, written
+//              to the workspace (fp32, base-2 logits).  One wave per (query
+//              head, context chunk), four waves of a K head's group per
+//              workgroup, so a K row is read from HBM once per group.
+//   2. local:  per (query head, range of kSelRows rows): the range's max and
+//              sum of 2^(s - max), and its own top_k rows (a row in the
+//              global top_k is in its range's top_k), kept in index order.
+//   3. gather: per query head: merge the ranges' (max, sum) into the full
+//              softmax normaliser, select the top_k among the candidates,
+//              read only those V rows and sum them with their weights.
+// Selection is an exact radix select on order-preserving 32-bit keys of the
+// fp32 logits (three digit passes of 11, 11 and 10 bits over a 2048-bin LDS
+// histogram) followed by an index-ordered compaction, so the chosen set is
+// the top_k by (logit, -row index) in the kernel's fp32 logits.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace dqkv {
+
+constexpr int kSelThreads = 256;
+constexpr int kBins = 2048;
+
+// Monotone map from fp32 to uint32 (a < b  <=>  key(a) < key(b)); -0 and +0
+// share the key of +0.  Logits here are always finite.
+__device__ __forceinline__ uint32_t order_key(float s) {
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Exclusive prefix sum of v over the 256 threads of the block, in thread
+// order; *total receives the block's sum.  Uses red[0..3]; ends synchronised.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) red[wave] = inc;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    const int t = red[w];
+    before += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + inc - v;
+}
+
+struct Threshold {
+  uint32_t key;  // the k-th largest key
+  int need_eq;   // rows with this key to take (the lowest-indexed ones)
+};
+
+// k-th largest of the n keys key(0..n-1), 1 <= k <= n, by radix select from
+// the most significant digit.  Invariant before each pass: the keys that
+// match the digits fixed so far number at least krem, and the keys above
+// that prefix number k - krem.  hist: kBins LDS words; red: 8 LDS ints.
+template <class KeyF>
+__device__ Threshold block_select_threshold(KeyF key, int n, int k, uint32_t* hist, int* red) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  int krem = k;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+    for (int d = tid; d < kBins; d += kSelThreads) hist[d] = 0u;
+    __syncthreads();
+    for (int x = tid; x < n; x += kSelThreads) {
+      const uint32_t kk = key(x);
+      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    // Thread t owns bins kBins-1-8t down to kBins-8-8t: bins in descending
+    // order across the block, so the exclusive scan counts the keys in
+    // higher bins.
+    constexpr int BPT = kBins / kSelThreads;
+    int cnt[BPT], own = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      cnt[e] = (int)hist[kBins - 1 - BPT * tid - e];
+      own += cnt[e];
+    }
+    int total;
+    const int above = block_exclusive_scan(own, red, &total);
+    if (above < krem && krem <= above + own) {  // exactly one thread
+      int run = above;
+#pragma unroll
+      for (int e = 0; e < BPT; ++e) {
+        if (run + cnt[e] >= krem) {
+          red[4] = kBins - 1 - BPT * tid - e;
+          red[5] = krem - run;
+          break;
+        }
+        run += cnt[e];
+      }
+    }
+    __syncthreads();
+    const uint32_t digit = (uint32_t)red[4];
+    krem = red[5];
+    prefix |= digit << shift;
+    pmask |= dmask << shift;
+  }
+  __syncthreads();  // red[4], red[5] are rewritten by the next caller
+  return Threshold{prefix, krem};
+}
+
+// Calls emit(pos, x) for the k selected positions x (key above the
+// threshold, or equal to it and among the first need_eq such in index
+// order), with pos = rank of x among the selected in index order.  Each wave
+// walks one contiguous quarter of [0, n) in 64-element steps.
+template <class KeyF, class EmitF>
+__device__ void block_compact(KeyF key, int n, Threshold th, int* red, EmitF emit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int seg = ((n + 4 * 64 - 1) / (4 * 64)) * 64;
+  const int lo = min(n, wave * seg), hi = min(n, lo + seg);
+  int gt = 0, eq = 0;
+  for (int x0 = lo; x0 < hi; x0 += 64) {
+    const int x = x0 + lane;
+    const uint32_t kk = x < hi ? key(x) : 0u;
+    gt += __popcll(__builtin_amdgcn_ballot_w64(x < hi && kk > th.key));
+    eq += __popcll(__builtin_amdgcn_ballot_w64(x < hi && kk == th.key));
+  }
+  if (lane == 0) {
+    red[wave] = gt;
+    red[4 + wave] = eq;
+  }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += red[w];
+    eq_before += red[4 + w];
+  }
+  __syncthreads();
+  int pos0 = gt_before + min(eq_before, th.need_eq);
+  const uint64_t below = lanes_below();
+  for (int x0 = lo; x0 < hi; x0 += 64) {
+    const int x = x0 + lane;
+    const uint32_t kk = x < hi ? key(x) : 0u;
+    const bool is_gt = x < hi && kk > th.key;
+    const bool is_eq = x < hi && kk == th.key;
+    const uint64_t emask = __builtin_amdgcn_ballot_w64(is_eq);
+    const bool take = is_gt || (is_eq && eq_before + __popcll(emask & below) < th.need_eq);
+    const uint64_t smask = __builtin_amdgcn_ballot_w64(take);
+    if (take) emit(pos0 + __popcll(smask & below), x);
+    pos0 += __popcll(smask);
+    eq_before += __popcll(emask);
+  }
+}
+
+__device__ __forceinline__ float block_max(float v, float* redf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_max(v);
+  if (lane == 0) redf[wave] = v;
+  __syncthreads();
+  v = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
+  __syncthreads();
+  return v;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* redf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum(v);
+  if (lane == 0) redf[wave] = v;
+  __syncthreads();
+  v = (redf[0] + redf[1]) + (redf[2] + redf[3]);
+  __syncthreads();
+  return v;
+}
+
+// ------------------------------------------------------------ 1. scores
+
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void sel_score_kernel(
+    const T* __restrict__ q, const T* kc, const int32_t* __restrict__ ctx_len,
+    float* __restrict__ scores, int n_q, int n_k, int l_cap, int max_ctx, int ld_s, int S,
+    float qscale, const T* __restrict__ k_new, T* kc_w) {
+  constexpr int EPL = Elem<T>::kPer16;
+  constexpr int LPR_K = DK / EPL;   // lanes per K row
+  constexpr int RPL_K = 64 / LPR_K; // K rows per wave load
+  constexpr int NK = 64 / RPL_K;    // wave loads per 64-row tile
+  static_assert(LPR_K >= 1 && LPR_K <= 32, "head dim");
+
+  const int c = blockIdx.x, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (i >= n_q) return;
+  int L = ctx_len[b];
+  L = max(0, min(L, min(max_ctx, l_cap)));
+  const int j0 = c * S;
+  if (j0 >= L) return;
+  const int rows = min(S, L - j0);
+  const int hk = (i * n_k) / n_q;
+
+  const int kl = lane % LPR_K, kr = lane / LPR_K;
+  float qf[EPL];
+  Elem<T>::unpack(load16(q + ((size_t)b * n_q + i) * DK + kl * EPL), qf);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qf[e] *= qscale;
+
+  const T* kp = kc + (((size_t)b * n_k + hk) * l_cap + j0) * DK + kl * EPL;
+  const bool fused = k_new != nullptr;
+  const int r_new = fused ? L - 1 - j0 : -1;
+  const T* kn = fused ? k_new + ((size_t)b * n_k + hk) * DK + kl * EPL : nullptr;
+  if (fused && r_new < rows && i % (n_q / n_k) == 0 && lane < LPR_K)
+    *reinterpret_cast<u32x4*>(kc_w + (((size_t)b * n_k + hk) * l_cap + L - 1) * DK + kl * EPL) =
+        load16(kn);
+
+  float* out = scores + ((size_t)b * n_q + i) * ld_s + j0;
+  const int my_row = kl * RPL_K + kr;
+  for (int t0 = 0; t0 < rows; t0 += 64) {
+    u32x4 kv[NK];
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int r = t0 + u * RPL_K + kr;
+      kv[u] = r >= rows ? u32x4{0u, 0u, 0u, 0u} : load16(r == r_new ? kn : kp + (size_t)r * DK);
+    }
+    float s_mine = 0.f;
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      float kf[EPL];
+      Elem<T>::unpack(kv[u], kf);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s = fmaf(qf[e], kf[e], s);
+      s = group_sum<LPR_K>(s);
+      s_mine = (u == kl) ? s : s_mine;
+    }
+    if (t0 + my_row < rows) out[t0 + my_row] = s_mine;
+  }
+}
+
+// ------------------------------------------------- 2. per-range selection
+
+__global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ ctx_len,
+    float* __restrict__ range_ml, float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
+    int n_q, int l_cap, int max_ctx, int ld_s, int n_ranges, int top_k) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ int red[8];
+  __shared__ float redf[4];
+  const int rg = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  int L = ctx_len[b];
+  L = max(0, min(L, min(max_ctx, l_cap)));
+  const int j0 = rg * kSelRows;
+  if (j0 >= L) return;
+  const int rows = min(kSelRows, L - j0);
+  const float* sc = scores + ((size_t)b * n_q + i) * ld_s + j0;
+
+  float m = -INFINITY;
+  for (int r = tid; r < rows; r += kSelThreads) m = fmaxf(m, sc[r]);
+  m = block_max(m, redf);
+  float l = 0.f;
+  for (int r = tid; r < rows; r += kSelThreads) l += fast_exp2(sc[r] - m);
+  l = block_sum(l, redf);
+  const size_t slot = ((size_t)b * n_q + i) * n_ranges + rg;
+  if (tid == 0) {
+    range_ml[2 * slot] = m;
+    range_ml[2 * slot + 1] = l;
+  }
+
+  float* cs = cand_s + slot * top_k;
+  int32_t* ci = cand_i + slot * top_k;
+  if (rows <= top_k) {  // the whole range is a candidate
+    for (int r = tid; r < rows; r += kSelThreads) {
+      cs[r] = sc[r];
+      ci[r] = j0 + r;
+    }
+    return;
+  }
+  auto key = [&](int r) { return order_key(sc[r]); };
+  const Threshold th = block_select_threshold(key, rows, top_k, hist, red);
+  block_compact(key, rows, th, red, [&](int pos, int r) {
+    if (pos < top_k) {
+      cs[pos] = sc[r];
+      ci[pos] = j0 + r;
+    }
+  });
+}
+
+// ------------------------------------------ 3. final selection and gather
+
+template <typename T, int DV>
+__global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
+    const T* vc, const int32_t* __restrict__ ctx_len, const float* __restrict__ range_ml,
+    const float* __restrict__ cand_s, const int32_t* __restrict__ cand_i, T* __restrict__ out,
+    float* __restrict__ lse, int32_t* __restrict__ sel_idx, int n_q, int n_v, int l_cap,
+    int max_ctx, int n_ranges, int top_k, const T* __restrict__ v_new, T* vc_w) {
+  constexpr int EPL = Elem<T>::kPer16;
+  constexpr int LPR = DV / EPL;               // lanes per V row
+  constexpr int RPP = kSelThreads / LPR;      // V rows per pass of the block
+  constexpr int U = 4;                        // row loads in flight per thread
+  __shared__ uint32_t hist[kBins];
+  __shared__ int red[8];
+  __shared__ float redf[4];
+  __shared__ int32_t sel_j[kMaxTopK];
+  __shared__ float sel_w[kMaxTopK];
+  __shared__ float part[RPP][DV + 4];
+
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  int L = ctx_len[b];
+  L = max(0, min(L, min(max_ctx, l_cap)));
+  const int hv = (i * n_v) / n_q;
+  const size_t head = (size_t)b * n_q + i;
+  const bool fused = v_new != nullptr;
+  const T* vn = fused ? v_new + ((size_t)b * n_v + hv) * DV : nullptr;
+  if (fused && L > 0 && i % (n_q / n_v) == 0 && tid < LPR)
+    *reinterpret_cast<u32x4*>(vc_w + (((size_t)b * n_v + hv) * l_cap + L - 1) * DV + tid * EPL) =
+        load16(vn + tid * EPL);
+
+  // Softmax normaliser over all L rows from the ranges' (max, sum).
+  const int nr = (L + kSelRows - 1) / kSelRows;
+  const float* ml = range_ml + head * n_ranges * 2;
+  float M = -INFINITY;
+  for (int r = tid; r < nr; r += kSelThreads) M = fmaxf(M, ml[2 * r]);
+  M = block_max(M, redf);
+  float Z = 0.f;
+  for (int r = tid; r < nr; r += kSelThreads) Z += fast_exp2(ml[2 * r] - M) * ml[2 * r + 1];
+  Z = block_sum(Z, redf);
+  const float invZ = L > 0 ? 1.f / Z : 0.f;
+
+  // Candidates: range r holds min(top_k, rows in r) entries at slot r * top_k;
+  // all ranges but the last are full, so position p of the concatenation is
+  // entry p % ck of range p / ck.
+  const int ck = min(top_k, kSelRows);
+  const int n_c = nr == 0 ? 0 : (nr - 1) * ck + min(top_k, L - (nr - 1) * kSelRows);
+  const int kk = min(top_k, L);
+  const float* cs = cand_s + head * n_ranges * top_k;
+  const int32_t* ci = cand_i + head * n_ranges * top_k;
+  auto at = [&](int p) { return (size_t)(p / ck) * top_k + p % ck; };
+  auto take = [&](int pos, int p) {
+    if (pos >= kk) return;
+    sel_j[pos] = ci[at(p)];
+    sel_w[pos] = fast_exp2(cs[at(p)] - M) * invZ;
+  };
+  if (n_c <= kk) {
+    for (int p = tid; p < n_c; p += kSelThreads) take(p, p);
+  } else {
+    auto key = [&](int p) { return order_key(cs[at(p)]); };
+    const Threshold th = block_select_threshold(key, n_c, kk, hist, red);
+    block_compact(key, n_c, th, red, take);
+  }
+  __syncthreads();
+  if (sel_idx != nullptr)
+    for (int p = tid; p < top_k; p += kSelThreads)
+      sel_idx[head * top_k + p] = p < kk ? sel_j[p] : -1;
+
+  // o = sum over the selected rows of w_j V_j: LPR lanes per row, RPP rows
+  // per pass, U passes' loads issued before their use.
+  const int vl = tid % LPR, vr = tid / LPR;
+  const T* vbase = vc + ((size_t)b * n_v + hv) * l_cap * DV + vl * EPL;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int r0 = vr; r0 < kk; r0 += U * RPP) {
+    u32x4 v[U];
+    float w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u * RPP;
+      w[u] = 0.f;
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      if (r < kk) {
+        const int j = sel_j[r];
+        w[u] = sel_w[r];
+        v[u] = (fused && j == L - 1) ? load16(vn + vl * EPL) : load16(vbase + (size_t)j * DV);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[EPL];
+      Elem<T>::unpack(v[u], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w[u], vf[e], acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) part[vr][vl * EPL + e] = acc[e];
+  __syncthreads();
+  for (int d = tid; d < DV; d += kSelThreads) {
+    float o = 0.f;
+    for (int r = 0; r < RPP; ++r) o += part[r][d];
+    out[head * DV + d] = Elem<T>::from_f32(o);
+  }
+  if (tid == 0 && lse != nullptr) lse[head] = L > 0 ? (M + fast_log2(Z)) * kLn2 : -INFINITY;
+}
+
+// ------------------------------------------------------------------ launch
+
+template <typename T, int DK>
+static hipError_t launch_score_t(const SelectiveArgs& a) {
+  dim3 grid(a.C, (a.n_q + 3) / 4, a.batch);
+  hipLaunchKernelGGL((sel_score_kernel<T, DK>), grid, dim3(256), 0, a.stream, (const T*)a.q,
+                     (const T*)a.k_cache, a.ctx_len, a.scores, a.n_q, a.n_k, a.l_cap,
+                     a.max_ctx, a.ld_s, a.S, a.scale * kLog2e, (const T*)a.k_new,
+                     (T*)a.k_cache);
+  return hipGetLastError();
+}
+
+template <typename T, int DV>
+static hipError_t launch_gather_t(const SelectiveArgs& a) {
+  hipLaunchKernelGGL((sel_gather_kernel<T, DV>), dim3(a.n_q, a.batch), dim3(kSelThreads), 0,
+                     a.stream, (const T*)a.v_cache, a.ctx_len, a.range_ml, a.cand_s, a.cand_i,
+                     (T*)a.out, a.lse, a.sel_idx, a.n_q, a.n_v, a.l_cap, a.max_ctx,
+                     a.n_ranges, a.top_k, (const T*)a.v_new, (T*)a.v_cache);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t score_dk(const SelectiveArgs& a) {
+  switch (a.d_k) {
+    case 32: return launch_score_t<T, 32>(a);
+    case 64: return launch_score_t<T, 64>(a);
+    case 128: return launch_score_t<T, 128>(a);
+    case 256:
+      if constexpr (sizeof(T) == 2) return launch_score_t<T, 256>(a);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t gather_dv(const SelectiveArgs& a) {
+  switch (a.d_v) {
+    case 32: return launch_gather_t<T, 32>(a);
+    case 64: return launch_gather_t<T, 64>(a);
+    case 128: return launch_gather_t<T, 128>(a);
+    case 256: return launch_gather_t<T, 256>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_selective(const SelectiveArgs& a) {
+  hipError_t e = a.bf16 ? score_dk<bf16>(a) : score_dk<float>(a);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sel_local_kernel, dim3(a.n_ranges, a.n_q, a.batch), dim3(kSelThreads), 0,
+                     a.stream, a.scores, a.ctx_len, a.range_ml, a.cand_s, a.cand_i, a.n_q,
+                     a.l_cap, a.max_ctx, a.ld_s, a.n_ranges, a.top_k);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return a.bf16 ? gather_dv<bf16>(a) : gather_dv<float>(a);
+}
+
+}  // namespace dqkv

@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--chunk", type=int, default=0, help="decode chunk rows (0 = auto)")
     p.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    p.add_argument("--selective-k", type=int, default=100,
+                   help="top_k of the selective-V decode leg (0 = skip it)")
     p.add_argument("--kernel-only", action="store_true",
                    help="only run steps (for profilers); skip twin, prefill, CPU baseline")
     p.add_argument("--ket", action="store_true",
@@ -173,6 +175,31 @@ class DecodeBench:
             self.ws.data_ptr(), self.ws_bytes, self._stream())
         assert st == 0, st
 
+    def setup_selective(self, top_k: int):
+        """Buffers of a selective-V decode step (diffqkv_decode_selective)."""
+        torch, dq = self.torch, self.dq
+        self.top_k = top_k
+        self.sel_ws_bytes = dq.selective_workspace_bytes(*self.shape, self.B, self.max_ctx, top_k)
+        self.sel_ws = torch.empty(self.sel_ws_bytes, dtype=torch.uint8, device="cuda")
+        self.sel_out = torch.empty_like(self.out)
+        n_q, n_k, n_v, d_k, d_v = self.shape
+        kk = sum(min(top_k, int(L)) for L in self.ctx)
+        self.sel_alg_bytes = (int(self.ctx.sum()) * n_k * d_k * self.esize   # all of K
+                              + n_q * kk * d_v * self.esize                   # chosen V rows
+                              + self.B * n_q * (d_k + d_v) * self.esize      # q, out
+                              + self.B * (n_k * d_k + n_v * d_v) * self.esize)  # appended rows
+        self.sel_ws_traffic = 2 * n_q * int(self.ctx.sum()) * 4   # logits written, re-read
+
+    def selective_step(self, r):
+        """One decode step with selective V: append, logits, top-k, gather."""
+        k, v = self.caches[r]
+        st = self.lib.diffqkv_decode_selective(
+            *self.shape, self.dtype_code, self.B, self.l_cap, self.max_ctx, self.case.scale,
+            self.top_k, self.q.data_ptr(), self.k_new.data_ptr(), self.v_new.data_ptr(),
+            k.data_ptr(), v.data_ptr(), self.ctx_t.data_ptr(), self.sel_out.data_ptr(),
+            self.lse.data_ptr(), None, self.sel_ws.data_ptr(), self.sel_ws_bytes, self._stream())
+        assert st == 0, st
+
     def step(self, r):
         """One decode step: append + attend + merge (diffqkv_decode_append)."""
         k, v = self.caches[r]
@@ -185,18 +212,19 @@ class DecodeBench:
 
     # -- timing -------------------------------------------------------------
 
-    def time_steps(self, steps: int, warmup: int, eager: bool = False):
+    def time_steps(self, steps: int, warmup: int, eager: bool = False, fn=None):
         """Average ms per step over exactly `steps` steps (graph replay)."""
         torch = self.torch
         R = self.replicas
+        fn = fn or self.step
         for w in range(warmup):
-            self.step(w % R)
+            fn(w % R)
         torch.cuda.synchronize()
         graphs = {}
         if not eager:
             try:
                 for n in {R, steps % R} - {0}:
-                    graphs[n] = self._graph(self.step, n)
+                    graphs[n] = self._graph(fn, n)
                 for g in graphs.values():  # warm replays
                     g.replay()
                 torch.cuda.synchronize()
@@ -213,7 +241,7 @@ class DecodeBench:
                 graphs[steps % R].replay()
         else:
             for s in range(steps):
-                self.step(s % R)
+                fn(s % R)
         t1.record()
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps, bool(graphs)
@@ -467,6 +495,17 @@ def main():
                        "combine": round(k_ms[1] * 1e3, 2)},
         "kernel_source_sha256": kernel_source_hash(),
     }
+    if args.selective_k > 0:
+        bench.setup_selective(args.selective_k)
+        ms_sel, _ = bench.time_steps(args.steps, args.warmup, args.eager, bench.selective_step)
+        log(f"selective-V step (top_k {args.selective_k}) {ms_sel * 1e3:.2f} us")
+        result["selective_v"] = {
+            "top_k": args.selective_k, "us_per_step": round(ms_sel * 1e3, 2),
+            "alg_bytes_per_step": bench.sel_alg_bytes,
+            "GBps": round(bench.sel_alg_bytes / (ms_sel * 1e-3) / 1e9, 1),
+            "workspace_bytes_per_step": bench.sel_ws_traffic,
+            "speedup_over_full_decode": round(ms / ms_sel, 3),
+            "step": "fused kv_append + logits + per-range top-k + final top-k and V gather"}
     sym_name = None if args.no_twin else (args.twin or TWINS.get(args.workload))
     asym_bytes = bench.alg_bytes_step
     bench.free()

@@ -213,6 +213,51 @@ int32_t diffqkv_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
                         void* out, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/*
+ * diffqkv_decode_selective -- decode with selective V fetching (architecture
+ * page, section "Selective V Cache Fetching"; a NEXT-step inference
+ * optimisation, not part of the Sigma model itself).
+ *
+ * For every sequence b and query head i the attention weights
+ * alpha_j = softmax_j(scale * q_i . K_j) are computed over all rows
+ * j < ctx_len[b] (the whole K cache is read), then only the V rows of the
+ * top_k largest weights are read and
+ *
+ *   out[b][i] = sum_{j in TopK} alpha_j * V[floor(i n_v / n_q)][j]
+ *
+ * with alpha the full softmax: the selected weights are not renormalised, so
+ * the output equals diffqkv_decode's when top_k >= ctx_len[b].  Equal
+ * weights are ordered by row index, lower first (the page leaves ties open).
+ * The selection is decided on the kernel's fp32 logits.
+ *
+ *   top_k     1 .. 1024 (the page's experiments use 100).
+ *   k_new, v_new  optional fused append as in diffqkv_decode_append (both or
+ *             neither): row ctx_len[b] - 1 is written from them first.
+ *   lse       optional [B][n_q] fp32: log-sum-exp over ALL visible rows.
+ *   sel_idx   optional [B][n_q][top_k] int32: the selected rows in ascending
+ *             order, -1 past min(top_k, ctx_len[b]).
+ *   workspace diffqkv_decode_selective_workspace bytes, 16-byte aligned,
+ *             contents need not be initialised; it holds the fp32 logits
+ *             ([B][n_q][max_ctx rounded up to 64]) and per-4096-row-range
+ *             candidates.
+ * ctx_len is clamped to [0, max_ctx]; ctx_len[b] = 0 gives out = 0,
+ * lse = -inf, sel_idx = -1.  Three kernels on `stream`: logits (reads K
+ * once), per-range top-k, final top-k with the V gather.
+ */
+int32_t diffqkv_decode_selective_workspace(int32_t n_q, int32_t n_k, int32_t n_v,
+                                           int32_t d_k, int32_t d_v, int32_t batch,
+                                           int32_t max_ctx, int32_t top_k,
+                                           size_t* bytes);
+
+int32_t diffqkv_decode_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                                 int32_t d_v, int32_t dtype, int32_t batch,
+                                 int32_t l_cap, int32_t max_ctx, float scale,
+                                 int32_t top_k, const void* q, const void* k_new,
+                                 const void* v_new, void* k_cache, void* v_cache,
+                                 const int32_t* ctx_len, void* out, float* lse,
+                                 int32_t* sel_idx, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

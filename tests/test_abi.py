@@ -164,3 +164,42 @@ def test_binding_refuses_cpu_tensors(lib):
     v = torch.zeros(1, 4, 8, 64)
     with pytest.raises(ValueError):
         dq.decode(q, k, v, torch.zeros(1, dtype=torch.int32))
+
+
+def test_selective_workspace_and_validation(lib):
+    def layout(B, n_q, ctx, k):
+        ld = max(64, -(-ctx // 64) * 64)
+        nr = max(1, -(-ctx // 4096))
+        a = lambda x: -(-x // 256) * 256
+        return a(B * n_q * ld * 4) + a(B * n_q * nr * 8) + a(B * n_q * nr * k * 4) + B * n_q * nr * k * 4
+
+    for B, n_q, ctx, k in [(1, 16, 32768, 100), (4, 16, 65536, 100), (3, 32, 5001, 1024),
+                           (2, 8, 0, 1)]:
+        assert dq.selective_workspace_bytes(n_q, 4 if n_q > 4 else 1, n_q, 64, 128, B, ctx,
+                                            k) == layout(B, n_q, ctx, k)
+    for k, code in [(0, SHAPE), (-3, SHAPE), (1025, UNSUP)]:
+        with pytest.raises(dq.DQKVError) as e:
+            dq.selective_workspace_bytes(16, 4, 16, 64, 128, 1, 1024, k)
+        assert e.value.status == code
+
+    need = layout(1, 16, 1024, 100)
+
+    def call(**kw):
+        a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=1, l_cap=1024,
+                 max_ctx=1024, scale=0.125, top_k=100, q=FAKE, kn=None, vn=None, kc=FAKE,
+                 vc=FAKE, ctx=FAKE, out=FAKE, lse=None, sel=None, ws=FAKE, ws_bytes=need)
+        a.update(kw)
+        return lib.diffqkv_decode_selective(
+            a["n_q"], a["n_k"], a["n_v"], a["d_k"], a["d_v"], a["dtype"], a["B"], a["l_cap"],
+            a["max_ctx"], a["scale"], a["top_k"], a["q"], a["kn"], a["vn"], a["kc"], a["vc"],
+            a["ctx"], a["out"], a["lse"], a["sel"], a["ws"], a["ws_bytes"], None)
+    assert call(n_k=3) == SHAPE
+    assert call(d_k=48) == UNSUP
+    assert call(top_k=0) == SHAPE and call(top_k=2000) == UNSUP
+    assert call(max_ctx=2048) == SHAPE
+    assert call(scale=-1.0) == SHAPE
+    assert call(kn=FAKE) == NULL          # k_new without v_new
+    assert call(out=None) == NULL and call(ws=None) == NULL
+    assert call(q=FAKE + 4) == ALIGN and call(kn=FAKE, vn=FAKE + 2) == ALIGN
+    assert call(ws_bytes=need - 1) == WS
+    assert call(B=0) == OK
