@@ -106,10 +106,20 @@ struct SelLayout {
   size_t off_ml, off_cs, off_ci, total;
 };
 
-int selective_layout(int n_q, int batch, int max_ctx, int top_k, SelLayout* o) {
+// Rows per logit-kernel workgroup (four waves, one 64-row tile each per
+// step): one tile per wave while that needs at most 8192 waves, more beyond.
+int plan_score_chunk(int n_k, int batch, int max_ctx) {
+  const long long tiles = ((long long)max_ctx + 63) / 64 * n_k * batch;
+  long long tpw = (tiles + 8191) / 8192;
+  if (tpw < 1) tpw = 1;
+  if (tpw > (1 << 20)) tpw = 1 << 20;
+  return (int)(256 * tpw);
+}
+
+int selective_layout(int n_q, int n_k, int batch, int max_ctx, int top_k, SelLayout* o) {
   if (top_k < 1) return DQKV_ERR_SHAPE;
   if (top_k > dqkv::kMaxTopK) return DQKV_ERR_UNSUPPORTED;
-  o->S = plan_chunk_h(n_q, 1, batch, max_ctx);
+  o->S = plan_score_chunk(n_k, batch, max_ctx);
   o->C = chunks_for(max_ctx, o->S);
   if (o->C > kMaxChunks) return DQKV_ERR_UNSUPPORTED;
   o->ld_s = (int)(((long long)max_ctx + 63) / 64 * 64);
@@ -372,7 +382,7 @@ int32_t diffqkv_decode_selective_workspace(int32_t n_q, int32_t n_k, int32_t n_v
   if (st) return st;
   if (batch < 0 || max_ctx < 0) return DQKV_ERR_SHAPE;
   SelLayout lay;
-  st = selective_layout(n_q, batch, max_ctx, top_k, &lay);
+  st = selective_layout(n_q, n_k, batch, max_ctx, top_k, &lay);
   if (st) return st;
   *bytes = lay.total;
   return DQKV_OK;
@@ -394,7 +404,7 @@ int32_t diffqkv_decode_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t 
     return DQKV_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return DQKV_ERR_SHAPE;
   SelLayout lay;
-  st = selective_layout(n_q, batch, max_ctx, top_k, &lay);
+  st = selective_layout(n_q, n_k, batch, max_ctx, top_k, &lay);
   if (st) return st;
   if (batch == 0) return DQKV_OK;
   if ((k_new == nullptr) != (v_new == nullptr)) return DQKV_ERR_NULL;

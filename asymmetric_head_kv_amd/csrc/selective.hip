@@ -188,9 +188,110 @@ __device__ __forceinline__ float block_sum(float v, float* redf) {
   return v;
 }
 
+// Register-resident variants for up to kSelThreads * E keys: wave w, lane l
+// holds elements w * 64 E + 64 e + l (e < E) in its registers, so each wave
+// owns a contiguous quarter and every load of a wave is 64 consecutive
+// elements.  One round of loads, then every pass works from registers.
+
+template <int E>
+__device__ __forceinline__ int reg_index(int e) {
+  return (threadIdx.x >> 6) * 64 * E + 64 * e + (threadIdx.x & 63);
+}
+
+template <int E>
+__device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k,
+                                          uint32_t* hist, int* red) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  int krem = k;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+    for (int d = tid; d < kBins; d += kSelThreads) hist[d] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (reg_index<E>(e) < n && (key[e] & pmask) == prefix)
+        atomicAdd(&hist[(key[e] >> shift) & dmask], 1u);
+    __syncthreads();
+    constexpr int BPT = kBins / kSelThreads;
+    int cnt[BPT], own = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      cnt[e] = (int)hist[kBins - 1 - BPT * tid - e];
+      own += cnt[e];
+    }
+    int total;
+    const int above = block_exclusive_scan(own, red, &total);
+    if (above < krem && krem <= above + own) {
+      int run = above;
+#pragma unroll
+      for (int e = 0; e < BPT; ++e) {
+        if (run + cnt[e] >= krem) {
+          red[4] = kBins - 1 - BPT * tid - e;
+          red[5] = krem - run;
+          break;
+        }
+        run += cnt[e];
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)red[4] << shift;
+    pmask |= dmask << shift;
+    krem = red[5];
+  }
+  __syncthreads();
+  return Threshold{prefix, krem};
+}
+
+// emit(pos, e) for every selected register slot e, pos = rank in index order.
+template <int E, class EmitF>
+__device__ __forceinline__ void reg_compact(const uint32_t (&key)[E], int n, Threshold th,
+                                            int* red, EmitF emit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool ok = reg_index<E>(e) < n;
+    gt += __popcll(__builtin_amdgcn_ballot_w64(ok && key[e] > th.key));
+    eq += __popcll(__builtin_amdgcn_ballot_w64(ok && key[e] == th.key));
+  }
+  if (lane == 0) {
+    red[wave] = gt;
+    red[4 + wave] = eq;
+  }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += red[w];
+    eq_before += red[4 + w];
+  }
+  __syncthreads();
+  int pos0 = gt_before + min(eq_before, th.need_eq);
+  const uint64_t below = lanes_below();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool ok = reg_index<E>(e) < n;
+    const bool is_gt = ok && key[e] > th.key;
+    const bool is_eq = ok && key[e] == th.key;
+    const uint64_t emask = __builtin_amdgcn_ballot_w64(is_eq);
+    const bool take = is_gt || (is_eq && eq_before + __popcll(emask & below) < th.need_eq);
+    const uint64_t smask = __builtin_amdgcn_ballot_w64(take);
+    if (take) emit(pos0 + __popcll(smask & below), e);
+    pos0 += __popcll(smask);
+    eq_before += __popcll(emask);
+  }
+}
+
+constexpr int kSelE = kSelRows / kSelThreads;  // keys per thread
+
 // ------------------------------------------------------------ 1. scores
 
-template <typename T, int DK>
+// One wave per 64-row tile and HW query heads that share one K head: each K
+// row the wave loads serves all HW heads, and the four waves of a workgroup
+// take different tiles, so all their loads are distinct.
+template <typename T, int DK, int HW>
 __global__ __launch_bounds__(256) void sel_score_kernel(
     const T* __restrict__ q, const T* kc, const int32_t* __restrict__ ctx_len,
     float* __restrict__ scores, int n_q, int n_k, int l_cap, int max_ctx, int ld_s, int S,
@@ -202,56 +303,70 @@ __global__ __launch_bounds__(256) void sel_score_kernel(
   static_assert(LPR_K >= 1 && LPR_K <= 32, "head dim");
 
   const int c = blockIdx.x, b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int i = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (i >= n_q) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = n_q / n_k, slices = G / HW;
+  const int hk = blockIdx.y / slices, slice = blockIdx.y % slices;
+  const int i0 = hk * G + slice * HW;
   int L = ctx_len[b];
   L = max(0, min(L, min(max_ctx, l_cap)));
   const int j0 = c * S;
   if (j0 >= L) return;
   const int rows = min(S, L - j0);
-  const int hk = (i * n_k) / n_q;
 
   const int kl = lane % LPR_K, kr = lane / LPR_K;
-  float qf[EPL];
-  Elem<T>::unpack(load16(q + ((size_t)b * n_q + i) * DK + kl * EPL), qf);
+  float qf[HW][EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) qf[e] *= qscale;
+  for (int h = 0; h < HW; ++h) {
+    Elem<T>::unpack(load16(q + ((size_t)b * n_q + i0 + h) * DK + kl * EPL), qf[h]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[h][e] *= qscale;
+  }
 
   const T* kp = kc + (((size_t)b * n_k + hk) * l_cap + j0) * DK + kl * EPL;
   const bool fused = k_new != nullptr;
-  const int r_new = fused ? L - 1 - j0 : -1;
+  const int r_new = fused ? L - 1 - j0 : -1;  // in [0, rows) iff this chunk owns it
   const T* kn = fused ? k_new + ((size_t)b * n_k + hk) * DK + kl * EPL : nullptr;
-  if (fused && r_new < rows && i % (n_q / n_k) == 0 && lane < LPR_K)
+  if (fused && r_new < rows && slice == 0 && wave == (r_new / 64) % 4 && lane < LPR_K)
     *reinterpret_cast<u32x4*>(kc_w + (((size_t)b * n_k + hk) * l_cap + L - 1) * DK + kl * EPL) =
         load16(kn);
 
-  float* out = scores + ((size_t)b * n_q + i) * ld_s + j0;
+  float* out = scores + ((size_t)b * n_q + i0) * ld_s + j0;
   const int my_row = kl * RPL_K + kr;
-  for (int t0 = 0; t0 < rows; t0 += 64) {
+  for (int t0 = wave * 64; t0 < rows; t0 += 256) {
     u32x4 kv[NK];
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       const int r = t0 + u * RPL_K + kr;
       kv[u] = r >= rows ? u32x4{0u, 0u, 0u, 0u} : load16(r == r_new ? kn : kp + (size_t)r * DK);
     }
-    float s_mine = 0.f;
+    float s_mine[HW];
+#pragma unroll
+    for (int h = 0; h < HW; ++h) s_mine[h] = 0.f;
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       float kf[EPL];
       Elem<T>::unpack(kv[u], kf);
-      float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s = fmaf(qf[e], kf[e], s);
-      s = group_sum<LPR_K>(s);
-      s_mine = (u == kl) ? s : s_mine;
+      for (int h = 0; h < HW; ++h) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s = fmaf(qf[h][e], kf[e], s);
+        s = group_sum<LPR_K>(s);
+        s_mine[h] = (u == kl) ? s : s_mine[h];
+      }
     }
-    if (t0 + my_row < rows) out[t0 + my_row] = s_mine;
+    if (t0 + my_row < rows) {
+#pragma unroll
+      for (int h = 0; h < HW; ++h) out[(size_t)h * ld_s + t0 + my_row] = s_mine[h];
+    }
   }
 }
 
 // ------------------------------------------------- 2. per-range selection
 
+// One workgroup per (query head, range of kSelRows rows); candidates of
+// range rg are written at [rg * top_k, rg * top_k + min(top_k, rows)), so a
+// head's candidate list is contiguous and in ascending row order.
 __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_len,
     float* __restrict__ range_ml, float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
@@ -260,7 +375,6 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
   __shared__ int red[8];
   __shared__ float redf[4];
   const int rg = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
   int L = ctx_len[b];
   L = max(0, min(L, min(max_ctx, l_cap)));
   const int j0 = rg * kSelRows;
@@ -268,14 +382,22 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
   const int rows = min(kSelRows, L - j0);
   const float* sc = scores + ((size_t)b * n_q + i) * ld_s + j0;
 
-  float m = -INFINITY;
-  for (int r = tid; r < rows; r += kSelThreads) m = fmaxf(m, sc[r]);
+  float s[kSelE];
+#pragma unroll
+  for (int e = 0; e < kSelE; ++e) {
+    const int x = reg_index<kSelE>(e);
+    s[e] = x < rows ? sc[x] : -INFINITY;
+  }
+  float m = s[0];
+#pragma unroll
+  for (int e = 1; e < kSelE; ++e) m = fmaxf(m, s[e]);
   m = block_max(m, redf);
   float l = 0.f;
-  for (int r = tid; r < rows; r += kSelThreads) l += fast_exp2(sc[r] - m);
+#pragma unroll
+  for (int e = 0; e < kSelE; ++e) l += reg_index<kSelE>(e) < rows ? fast_exp2(s[e] - m) : 0.f;
   l = block_sum(l, redf);
   const size_t slot = ((size_t)b * n_q + i) * n_ranges + rg;
-  if (tid == 0) {
+  if (threadIdx.x == 0) {
     range_ml[2 * slot] = m;
     range_ml[2 * slot + 1] = l;
   }
@@ -283,18 +405,24 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
   float* cs = cand_s + slot * top_k;
   int32_t* ci = cand_i + slot * top_k;
   if (rows <= top_k) {  // the whole range is a candidate
-    for (int r = tid; r < rows; r += kSelThreads) {
-      cs[r] = sc[r];
-      ci[r] = j0 + r;
+#pragma unroll
+    for (int e = 0; e < kSelE; ++e) {
+      const int x = reg_index<kSelE>(e);
+      if (x < rows) {
+        cs[x] = s[e];
+        ci[x] = j0 + x;
+      }
     }
     return;
   }
-  auto key = [&](int r) { return order_key(sc[r]); };
-  const Threshold th = block_select_threshold(key, rows, top_k, hist, red);
-  block_compact(key, rows, th, red, [&](int pos, int r) {
+  uint32_t key[kSelE];
+#pragma unroll
+  for (int e = 0; e < kSelE; ++e) key[e] = order_key(s[e]);
+  const Threshold th = reg_select_threshold<kSelE>(key, rows, top_k, hist, red);
+  reg_compact<kSelE>(key, rows, th, red, [&](int pos, int e) {
     if (pos < top_k) {
-      cs[pos] = sc[r];
-      ci[pos] = j0 + r;
+      cs[pos] = s[e];
+      ci[pos] = j0 + reg_index<kSelE>(e);
     }
   });
 }
@@ -310,7 +438,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
   constexpr int EPL = Elem<T>::kPer16;
   constexpr int LPR = DV / EPL;               // lanes per V row
   constexpr int RPP = kSelThreads / LPR;      // V rows per pass of the block
-  constexpr int U = 4;                        // row loads in flight per thread
+  constexpr int U = 128 / RPP < 1 ? 1 : (128 / RPP > 8 ? 8 : 128 / RPP);  // passes in flight
   __shared__ uint32_t hist[kBins];
   __shared__ int red[8];
   __shared__ float redf[4];
@@ -330,8 +458,27 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
     *reinterpret_cast<u32x4*>(vc_w + (((size_t)b * n_v + hv) * l_cap + L - 1) * DV + tid * EPL) =
         load16(vn + tid * EPL);
 
-  // Softmax normaliser over all L rows from the ranges' (max, sum).
+  // Candidates: range r contributed min(top_k, rows of r) entries at
+  // [r * top_k, ...); all ranges but the last are full, so the n_c entries
+  // are contiguous and in ascending row order.
   const int nr = (L + kSelRows - 1) / kSelRows;
+  const int n_c = nr == 0 ? 0 : (nr - 1) * top_k + min(top_k, L - (nr - 1) * kSelRows);
+  const int kk = min(top_k, L);
+  const float* cs = cand_s + head * n_ranges * top_k;
+  const int32_t* ci = cand_i + head * n_ranges * top_k;
+  const bool in_regs = n_c <= kSelRows;
+  float s[kSelE];
+  int32_t idx[kSelE];
+  if (in_regs) {
+#pragma unroll
+    for (int e = 0; e < kSelE; ++e) {
+      const int p = reg_index<kSelE>(e);
+      s[e] = p < n_c ? cs[p] : -INFINITY;
+      idx[e] = p < n_c ? ci[p] : 0;
+    }
+  }
+
+  // Softmax normaliser over all L rows from the ranges' (max, sum).
   const float* ml = range_ml + head * n_ranges * 2;
   float M = -INFINITY;
   for (int r = tid; r < nr; r += kSelThreads) M = fmaxf(M, ml[2 * r]);
@@ -341,24 +488,32 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
   Z = block_sum(Z, redf);
   const float invZ = L > 0 ? 1.f / Z : 0.f;
 
-  // Candidates: range r holds min(top_k, rows in r) entries at slot r * top_k;
-  // all ranges but the last are full, so position p of the concatenation is
-  // entry p % ck of range p / ck.
-  const int ck = min(top_k, kSelRows);
-  const int n_c = nr == 0 ? 0 : (nr - 1) * ck + min(top_k, L - (nr - 1) * kSelRows);
-  const int kk = min(top_k, L);
-  const float* cs = cand_s + head * n_ranges * top_k;
-  const int32_t* ci = cand_i + head * n_ranges * top_k;
-  auto at = [&](int p) { return (size_t)(p / ck) * top_k + p % ck; };
-  auto take = [&](int pos, int p) {
-    if (pos >= kk) return;
-    sel_j[pos] = ci[at(p)];
-    sel_w[pos] = fast_exp2(cs[at(p)] - M) * invZ;
-  };
-  if (n_c <= kk) {
-    for (int p = tid; p < n_c; p += kSelThreads) take(p, p);
-  } else {
-    auto key = [&](int p) { return order_key(cs[at(p)]); };
+  if (in_regs) {
+    auto take = [&](int pos, int e) {
+      if (pos < kk) {
+        sel_j[pos] = idx[e];
+        sel_w[pos] = fast_exp2(s[e] - M) * invZ;
+      }
+    };
+    if (n_c <= kk) {
+#pragma unroll
+      for (int e = 0; e < kSelE; ++e)
+        if (reg_index<kSelE>(e) < n_c) take(reg_index<kSelE>(e), e);
+    } else {
+      uint32_t key[kSelE];
+#pragma unroll
+      for (int e = 0; e < kSelE; ++e) key[e] = order_key(s[e]);
+      const Threshold th = reg_select_threshold<kSelE>(key, n_c, kk, hist, red);
+      reg_compact<kSelE>(key, n_c, th, red, take);
+    }
+  } else {  // more candidates than registers hold: passes over global memory
+    auto take = [&](int pos, int p) {
+      if (pos < kk) {
+        sel_j[pos] = ci[p];
+        sel_w[pos] = fast_exp2(cs[p] - M) * invZ;
+      }
+    };
+    auto key = [&](int p) { return order_key(cs[p]); };
     const Threshold th = block_select_threshold(key, n_c, kk, hist, red);
     block_compact(key, n_c, th, red, take);
   }
@@ -368,7 +523,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
       sel_idx[head * top_k + p] = p < kk ? sel_j[p] : -1;
 
   // o = sum over the selected rows of w_j V_j: LPR lanes per row, RPP rows
-  // per pass, U passes' loads issued before their use.
+  // per pass, the loads of U passes issued before their use.
   const int vl = tid % LPR, vr = tid / LPR;
   const T* vbase = vc + ((size_t)b * n_v + hv) * l_cap * DV + vl * EPL;
   float acc[EPL];
@@ -409,14 +564,40 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
 
 // ------------------------------------------------------------------ launch
 
-template <typename T, int DK>
-static hipError_t launch_score_t(const SelectiveArgs& a) {
-  dim3 grid(a.C, (a.n_q + 3) / 4, a.batch);
-  hipLaunchKernelGGL((sel_score_kernel<T, DK>), grid, dim3(256), 0, a.stream, (const T*)a.q,
+// Query heads per score wave: the largest of 8, 4, 2, 1 dividing n_q / n_k
+// (at most 2 when a tile's K loads already take 32 registers per lane).
+static int score_heads_per_wave(const SelectiveArgs& a, int nk_loads) {
+  const int G = a.n_q / a.n_k;
+  const int cap = nk_loads >= 32 ? 2 : 8;
+  for (int hw = cap; hw > 1; hw >>= 1)
+    if (G % hw == 0) return hw;
+  return 1;
+}
+
+template <typename T, int DK, int HW>
+static hipError_t launch_score_hw(const SelectiveArgs& a) {
+  dim3 grid(a.C, a.n_k * (a.n_q / a.n_k / HW), a.batch);
+  hipLaunchKernelGGL((sel_score_kernel<T, DK, HW>), grid, dim3(256), 0, a.stream, (const T*)a.q,
                      (const T*)a.k_cache, a.ctx_len, a.scores, a.n_q, a.n_k, a.l_cap,
                      a.max_ctx, a.ld_s, a.S, a.scale * kLog2e, (const T*)a.k_new,
                      (T*)a.k_cache);
   return hipGetLastError();
+}
+
+template <typename T, int DK>
+static hipError_t launch_score_t(const SelectiveArgs& a) {
+  constexpr int NK = DK / Elem<T>::kPer16;
+  switch (score_heads_per_wave(a, NK)) {
+    case 8:
+      if constexpr (NK < 32) return launch_score_hw<T, DK, 8>(a);
+      break;
+    case 4:
+      if constexpr (NK < 32) return launch_score_hw<T, DK, 4>(a);
+      break;
+    case 2: return launch_score_hw<T, DK, 2>(a);
+    case 1: return launch_score_hw<T, DK, 1>(a);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int DV>
