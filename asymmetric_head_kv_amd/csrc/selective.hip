@@ -8,9 +8,10 @@
 //
 // Three kernels, each one pass:
 //   1. score:  s_ij = (scale log2 e) q_i . K_j for every visible row, written
-//              to the workspace (fp32, base-2 logits).  One wave per (query
-//              head, context chunk), four waves of a K head's group per
-//              workgroup, so a K row is read from HBM once per group.
+//              to the workspace (fp32, base-2 logits).  A wave takes one
+//              64-row tile of a K head and all the query heads that share it
+//              (up to 16), so every K row is read once; bf16 products run on
+//              the matrix cores, fp32 ones on the vector ALUs.
 //   2. local:  per (query head, range of kSelRows rows): the range's max and
 //              sum of 2^(s - max), and its own top_k rows (a row in the
 //              global top_k is in its range's top_k), kept in index order.
@@ -168,26 +169,6 @@ __device__ void block_compact(KeyF key, int n, Threshold th, int* red, EmitF emi
   }
 }
 
-__device__ __forceinline__ float block_max(float v, float* redf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_max(v);
-  if (lane == 0) redf[wave] = v;
-  __syncthreads();
-  v = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
-  __syncthreads();
-  return v;
-}
-
-__device__ __forceinline__ float block_sum(float v, float* redf) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_sum(v);
-  if (lane == 0) redf[wave] = v;
-  __syncthreads();
-  v = (redf[0] + redf[1]) + (redf[2] + redf[3]);
-  __syncthreads();
-  return v;
-}
-
 // Register-resident variants for up to kSelThreads * E keys: wave w, lane l
 // holds elements w * 64 E + 64 e + l (e < E) in its registers, so each wave
 // owns a contiguous quarter and every load of a wave is 64 consecutive
@@ -198,6 +179,8 @@ __device__ __forceinline__ int reg_index(int e) {
   return (threadIdx.x >> 6) * 64 * E + 64 * e + (threadIdx.x & 63);
 }
 
+// hist: three kBins-word histograms (one per digit pass), zeroed and made
+// visible by a barrier before the call.
 template <int E>
 __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k,
                                           uint32_t* hist, int* red) {
@@ -208,18 +191,17 @@ __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-    for (int d = tid; d < kBins; d += kSelThreads) hist[d] = 0u;
-    __syncthreads();
+    uint32_t* h = hist + pass * kBins;
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (reg_index<E>(e) < n && (key[e] & pmask) == prefix)
-        atomicAdd(&hist[(key[e] >> shift) & dmask], 1u);
+        atomicAdd(&h[(key[e] >> shift) & dmask], 1u);
     __syncthreads();
     constexpr int BPT = kBins / kSelThreads;
     int cnt[BPT], own = 0;
 #pragma unroll
     for (int e = 0; e < BPT; ++e) {
-      cnt[e] = (int)hist[kBins - 1 - BPT * tid - e];
+      cnt[e] = (int)h[kBins - 1 - BPT * tid - e];
       own += cnt[e];
     }
     int total;
@@ -243,6 +225,11 @@ __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k
   }
   __syncthreads();
   return Threshold{prefix, krem};
+}
+
+__device__ __forceinline__ void clear_hists(uint32_t* hist) {
+  u32x4* h = reinterpret_cast<u32x4*>(hist);
+  for (int x = threadIdx.x; x < 3 * kBins / 4; x += kSelThreads) h[x] = u32x4{0u, 0u, 0u, 0u};
 }
 
 // emit(pos, e) for every selected register slot e, pos = rank in index order.
@@ -288,9 +275,10 @@ constexpr int kSelE = kSelRows / kSelThreads;  // keys per thread
 
 // ------------------------------------------------------------ 1. scores
 
-// One wave per 64-row tile and HW query heads that share one K head: each K
-// row the wave loads serves all HW heads, and the four waves of a workgroup
-// take different tiles, so all their loads are distinct.
+// fp32 logits on the vector ALUs (fp32 caches).  One wave per 64-row tile
+// and HW query heads that share one K head: each K row the wave loads serves
+// all HW heads, and the four waves of a workgroup take different tiles, so
+// all their loads are distinct.
 template <typename T, int DK, int HW>
 __global__ __launch_bounds__(256) void sel_score_kernel(
     const T* __restrict__ q, const T* kc, const int32_t* __restrict__ ctx_len,
@@ -362,6 +350,83 @@ __global__ __launch_bounds__(256) void sel_score_kernel(
   }
 }
 
+typedef __bf16 sel_bf16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 logits on the matrix cores.  For each 16-row block of a 64-row tile,
+// S^T[16 rows][16 heads] = K[16 rows][DK] . Q^T[DK][16 heads], in DK / 32
+// v_mfma_f32_16x16x32_bf16 steps.  Operand layouts: A lane l = K row l % 16,
+// elements 8 (l / 16) .. +7 of a 32-wide k block (one 16-byte load straight
+// from memory); B lane l = query head l % 16, the same k elements; D lane l
+// = head l % 16, rows 4 (l / 16) .. +3 of the block.  Up to 16 query heads
+// that share the K head ride on one product; the four waves of a workgroup
+// take different tiles.  The logits are the exact bf16 products summed in
+// fp32 by the matrix core, then scaled by scale * log2 e.
+template <int DK>
+__global__ __launch_bounds__(256) void sel_score_mfma_kernel(
+    const bf16* __restrict__ q, const bf16* kc, const int32_t* __restrict__ ctx_len,
+    float* __restrict__ scores, int n_q, int n_k, int l_cap, int max_ctx, int ld_s, int S,
+    float qscale, const bf16* __restrict__ k_new, bf16* kc_w) {
+  constexpr int KB = DK / 32;  // k blocks per row
+  const int c = blockIdx.x, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = n_q / n_k, slices = (G + 15) / 16;
+  const int hk = blockIdx.y / slices, slice = blockIdx.y % slices;
+  const int h0 = slice * 16, nh = min(16, G - h0);
+  const int i0 = hk * G + h0;
+  int L = ctx_len[b];
+  L = max(0, min(L, min(max_ctx, l_cap)));
+  const int j0 = c * S;
+  if (j0 >= L) return;
+  const int rows = min(S, L - j0);
+
+  const int l16 = lane & 15, kg = lane >> 4;
+  sel_bf16x8 qb[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    qb[kb] = __builtin_bit_cast(
+        sel_bf16x8, l16 < nh ? load16(q + ((size_t)b * n_q + i0 + l16) * DK + kb * 32 + 8 * kg)
+                             : u32x4{0u, 0u, 0u, 0u});
+
+  const bf16* kp = kc + (((size_t)b * n_k + hk) * l_cap + j0) * DK + 8 * kg;
+  const bool fused = k_new != nullptr;
+  const int r_new = fused ? L - 1 - j0 : -1;  // in [0, rows) iff this chunk owns it
+  const bf16* kn = fused ? k_new + ((size_t)b * n_k + hk) * DK + 8 * kg : nullptr;
+  if (fused && r_new < rows && slice == 0 && wave == (r_new / 64) % 4 && lane < DK / 8)
+    *reinterpret_cast<u32x4*>(kc_w + (((size_t)b * n_k + hk) * l_cap + L - 1) * DK + 8 * lane) =
+        load16(k_new + ((size_t)b * n_k + hk) * DK + 8 * lane);
+
+  float* out = scores + ((size_t)b * n_q + i0 + l16) * ld_s + j0;
+  for (int t0 = wave * 64; t0 < rows; t0 += 256) {
+    u32x4 kv[4][KB];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = t0 + rb * 16 + l16;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        kv[rb][kb] = r >= rows ? u32x4{0u, 0u, 0u, 0u}
+                               : load16((r == r_new ? kn : kp + (size_t)r * DK) + kb * 32);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(sel_bf16x8, kv[rb][kb]),
+                                                      qb[kb], acc, 0, 0, 0);
+      const int r = t0 + rb * 16 + 4 * kg;
+      if (l16 < nh) {
+        if (r + 3 < rows) {
+          *reinterpret_cast<f32x4*>(out + r) = acc * qscale;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (r + e < rows) out[r + e] = acc[e] * qscale;
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------- 2. per-range selection
 
 // One workgroup per (query head, range of kSelRows rows); candidates of
@@ -371,10 +436,11 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_len,
     float* __restrict__ range_ml, float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
     int n_q, int l_cap, int max_ctx, int ld_s, int n_ranges, int top_k) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ __align__(16) uint32_t hist[3 * kBins];
   __shared__ int red[8];
-  __shared__ float redf[4];
+  __shared__ float wm[4], wl[4];
   const int rg = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int L = ctx_len[b];
   L = max(0, min(L, min(max_ctx, l_cap)));
   const int j0 = rg * kSelRows;
@@ -388,18 +454,28 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
     const int x = reg_index<kSelE>(e);
     s[e] = x < rows ? sc[x] : -INFINITY;
   }
+  clear_hists(hist);
+  // The range's max and sum of 2^(s - max): per wave, then over the waves.
   float m = s[0];
 #pragma unroll
   for (int e = 1; e < kSelE; ++e) m = fmaxf(m, s[e]);
-  m = block_max(m, redf);
+  m = wave_max(m);
   float l = 0.f;
 #pragma unroll
   for (int e = 0; e < kSelE; ++e) l += reg_index<kSelE>(e) < rows ? fast_exp2(s[e] - m) : 0.f;
-  l = block_sum(l, redf);
+  l = wave_sum(l);
+  if (lane == 0) {
+    wm[wave] = m;
+    wl[wave] = l;
+  }
+  __syncthreads();
   const size_t slot = ((size_t)b * n_q + i) * n_ranges + rg;
   if (threadIdx.x == 0) {
-    range_ml[2 * slot] = m;
-    range_ml[2 * slot + 1] = l;
+    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+    float Z = 0.f;
+    for (int w = 0; w < 4; ++w) Z += wl[w] > 0.f ? wl[w] * fast_exp2(wm[w] - M) : 0.f;
+    range_ml[2 * slot] = M;
+    range_ml[2 * slot + 1] = Z;
   }
 
   float* cs = cand_s + slot * top_k;
@@ -439,9 +515,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
   constexpr int LPR = DV / EPL;               // lanes per V row
   constexpr int RPP = kSelThreads / LPR;      // V rows per pass of the block
   constexpr int U = 128 / RPP < 1 ? 1 : (128 / RPP > 8 ? 8 : 128 / RPP);  // passes in flight
-  __shared__ uint32_t hist[kBins];
+  __shared__ __align__(16) uint32_t hist[3 * kBins];
   __shared__ int red[8];
-  __shared__ float redf[4];
   __shared__ int32_t sel_j[kMaxTopK];
   __shared__ float sel_w[kMaxTopK];
   __shared__ float part[RPP][DV + 4];
@@ -478,15 +553,19 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
     }
   }
 
-  // Softmax normaliser over all L rows from the ranges' (max, sum).
+  clear_hists(hist);
+  // Softmax normaliser over all L rows from the ranges' (max, sum); every
+  // wave computes it alike, so no barrier is needed.
   const float* ml = range_ml + head * n_ranges * 2;
+  const int lane = tid & 63;
   float M = -INFINITY;
-  for (int r = tid; r < nr; r += kSelThreads) M = fmaxf(M, ml[2 * r]);
-  M = block_max(M, redf);
+  for (int r = lane; r < nr; r += 64) M = fmaxf(M, ml[2 * r]);
+  M = wave_max(M);
   float Z = 0.f;
-  for (int r = tid; r < nr; r += kSelThreads) Z += fast_exp2(ml[2 * r] - M) * ml[2 * r + 1];
-  Z = block_sum(Z, redf);
+  for (int r = lane; r < nr; r += 64) Z += fast_exp2(ml[2 * r] - M) * ml[2 * r + 1];
+  Z = wave_sum(Z);
   const float invZ = L > 0 ? 1.f / Z : 0.f;
+  __syncthreads();  // histograms cleared
 
   if (in_regs) {
     auto take = [&](int pos, int e) {
@@ -609,17 +688,35 @@ static hipError_t launch_gather_t(const SelectiveArgs& a) {
   return hipGetLastError();
 }
 
+template <int DK>
+static hipError_t launch_score_mfma(const SelectiveArgs& a) {
+  const int slices = (a.n_q / a.n_k + 15) / 16;
+  dim3 grid(a.C, a.n_k * slices, a.batch);
+  hipLaunchKernelGGL((sel_score_mfma_kernel<DK>), grid, dim3(256), 0, a.stream, (const bf16*)a.q,
+                     (const bf16*)a.k_cache, a.ctx_len, a.scores, a.n_q, a.n_k, a.l_cap,
+                     a.max_ctx, a.ld_s, a.S, a.scale * kLog2e, (const bf16*)a.k_new,
+                     (bf16*)a.k_cache);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t score_dk(const SelectiveArgs& a) {
-  switch (a.d_k) {
-    case 32: return launch_score_t<T, 32>(a);
-    case 64: return launch_score_t<T, 64>(a);
-    case 128: return launch_score_t<T, 128>(a);
-    case 256:
-      if constexpr (sizeof(T) == 2) return launch_score_t<T, 256>(a);
-      break;
+  if constexpr (sizeof(T) == 2) {
+    switch (a.d_k) {
+      case 32: return launch_score_mfma<32>(a);
+      case 64: return launch_score_mfma<64>(a);
+      case 128: return launch_score_mfma<128>(a);
+      case 256: return launch_score_mfma<256>(a);
+    }
+    return hipErrorInvalidValue;
+  } else {
+    switch (a.d_k) {
+      case 32: return launch_score_t<T, 32>(a);
+      case 64: return launch_score_t<T, 64>(a);
+      case 128: return launch_score_t<T, 128>(a);
+    }
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
 }
 
 template <typename T>

@@ -103,6 +103,9 @@ SMALL = [
     ("bf16", 8, 2, 8, 256, 32, [1500], 1536),
     ("f32", 8, 2, 4, 64, 64, [4500, 64], 4608),
     ("f32", 4, 1, 4, 32, 256, [300], 320),
+    # 24 query heads on one K head: two groups of query heads (16 + 8) per
+    # K tile in the bf16 logit kernel.
+    ("bf16", 24, 1, 8, 32, 64, [3000, 2999], 3008),
     # 5 ranges: with top_k = 1024 the 5120 candidates exceed what the final
     # selection holds in registers and it takes its global-memory passes.
     ("bf16", 8, 2, 8, 64, 128, [20000], 20032),
