@@ -5,9 +5,9 @@ leg; never by the GPU library.
 """
 
 from .attention import (attend_one, attend_selective_one, attention_weights, decode,
-                        decode_selective, default_scale, group_sharing_index, kv_append,
-                        prefill, top_k_rows)
+                        decode_paged, decode_selective, default_scale, group_sharing_index,
+                        kv_append, kv_group_sharing, paged_to_contiguous, prefill, top_k_rows)
 
 __all__ = ["attend_one", "attend_selective_one", "attention_weights", "decode",
-           "decode_selective", "default_scale", "group_sharing_index", "kv_append",
-           "prefill", "top_k_rows"]
+           "decode_paged", "decode_selective", "default_scale", "group_sharing_index",
+           "kv_append", "kv_group_sharing", "paged_to_contiguous", "prefill", "top_k_rows"]

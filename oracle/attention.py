@@ -27,7 +27,9 @@ Readings taken where the pages are silent (all listed in the design doc):
 
 Selective-V decode (architecture page, "Selective V Cache Fetching") keeps
 the full softmax weights and sums only the V rows of the k largest; ties go
-to the lower row index (a reading: the page does not say).
+to the lower row index (a reading: the page does not say).  Two layouts are
+defined as copies: the kv_group_sharing expansion (FlexHeadFA section) and a
+paged cache with separate K and V page pools under one block table.
 
 Pins (tests/test_oracle.py): the FlexHeadFA index worked example, reduction
 to textbook MHA / GQA / MQA (torch's scaled_dot_product_attention in fp64),
@@ -36,7 +38,10 @@ the kv_group_sharing equivalence, closed forms (one key, zero scale, two keys
 with chosen logits), key-permutation invariance, prefill/decode consistency
 and causal masking, Step 2's concatenation for the append, and for
 selective V: k >= L equals full decode, k = 1 is the arg-max row times its
-weight, brute force on tiny shapes, and ties resolved to lower indices.
+weight, brute force on tiny shapes, and ties resolved to lower indices; for
+the layouts: attention unchanged under kv_group_sharing (both directions),
+the page's 4 -> 16 replication count, and paged gather / scatter round trips
+with decode over shuffled pages equal to decode over the contiguous cache.
 """
 
 from __future__ import annotations
@@ -215,3 +220,58 @@ def decode_selective(q, k_cache, v_cache, ctx_len, top_k: int, scale: float | No
             out[b, i], selected[b][i] = attend_selective_one(
                 q[b, i], k_cache[b, g, :L], v_cache[b, hv, :L], scale, top_k)
     return out, selected
+
+
+def kv_group_sharing(k_cache, v_cache):
+    """The compatibility expansion for frameworks that need n_k = n_v.
+
+    Architecture page, FlexHeadFA section (the kv_group_sharing wrapper of
+    the paper's Appendix E): the side with fewer heads is duplicated up to
+    the other's head count -- with n_k < n_v each K head is repeated
+    n_v / n_k times, with n_k > n_v each V head n_k / n_v times.  Expanded
+    head h' copies original head floor(h' * n_small / n_large), i.e. the
+    copies of one head are adjacent, which is the order under which the
+    query-head maps of both layouts pick the same rows (pinned by the
+    decode-equivalence test).  A pure copy of raw storage.
+    """
+    k = np.asarray(k_cache)
+    v = np.asarray(v_cache)
+    n_k, n_v = k.shape[1], v.shape[1]
+    n_h = max(n_k, n_v)
+    k_idx = [group_sharing_index(h, n_h, n_k) for h in range(n_h)]
+    v_idx = [group_sharing_index(h, n_h, n_v) for h in range(n_h)]
+    return k[:, k_idx].copy(), v[:, v_idx].copy()
+
+
+def paged_to_contiguous(k_pages, v_pages, block_table, ctx_len, l_cap=None):
+    """Gather a paged cache into the contiguous head-major layout.
+
+    Definition of the paged layout (a serving layout, not on the pages: the
+    architecture page names vLLM's paged attention as prior art that treats
+    K and V alike; here K and V keep separate page pools with their own row
+    shapes and share one block table): row j of sequence b lives in page
+    block_table[b][j // P], slot j % P, where P is the page size in rows;
+    ``k_pages[num_pages][n_k][P][d_k]``, ``v_pages[num_pages][n_v][P][d_v]``.
+    Rows at or past ctx_len[b] are left as zeros.  A pure copy.
+    """
+    kp = np.asarray(k_pages)
+    vp = np.asarray(v_pages)
+    table = np.asarray(block_table)
+    B = table.shape[0]
+    P = kp.shape[2]
+    if l_cap is None:
+        l_cap = max([int(x) for x in ctx_len] + [1])
+    k = np.zeros((B, kp.shape[1], l_cap, kp.shape[3]), dtype=kp.dtype)
+    v = np.zeros((B, vp.shape[1], l_cap, vp.shape[3]), dtype=vp.dtype)
+    for b in range(B):
+        for j in range(int(ctx_len[b])):
+            page = int(table[b, j // P])
+            k[b, :, j, :] = kp[page, :, j % P, :]
+            v[b, :, j, :] = vp[page, :, j % P, :]
+    return k, v
+
+
+def decode_paged(q, k_pages, v_pages, block_table, ctx_len, scale: float | None = None):
+    """Decode over a paged cache: :func:`decode` on the gathered rows."""
+    k, v = paged_to_contiguous(k_pages, v_pages, block_table, ctx_len)
+    return decode(q, k, v, ctx_len, scale)

@@ -183,6 +183,65 @@ def test_kv_group_sharing_equivalence():
     b, lb = oracle.decode(q, k_dup, v, lens)
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(la, lb)
+    # The oracle's expansion is that duplication, and (SIGMA's 4 -> 16) it
+    # repeats each K head four times; V is untouched.
+    k_exp, v_exp = oracle.kv_group_sharing(k, v)
+    np.testing.assert_array_equal(k_exp, k_dup)
+    np.testing.assert_array_equal(v_exp, v)
+    assert k_exp.shape[1] == 16 and all(
+        (k_exp[:, 4 * g + r] == k[:, g]).all() for g in range(4) for r in range(4))
+
+
+@pytest.mark.parametrize("heads", [(12, 2, 6), (8, 8, 2), (6, 3, 6), (8, 4, 1)])
+def test_kv_group_sharing_leaves_attention_unchanged(heads):
+    # Either side may be the smaller one: expanding it must not change the
+    # output of any query head (the wrapper's purpose, FlexHeadFA section).
+    n_q, n_k, n_v = heads
+    q, k, v, lens = _case(21, 2, n_q, n_k, n_v, 16, 8, 33)
+    k_exp, v_exp = oracle.kv_group_sharing(k, v)
+    assert k_exp.shape[1] == v_exp.shape[1] == max(n_k, n_v)
+    a, la = oracle.decode(q, k, v, lens)
+    b, lb = oracle.decode(q, k_exp, v_exp, lens)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(la, lb)
+
+
+def _to_pages(k, v, lens, P, seed):
+    """Scatter contiguous caches into shuffled pages (test helper)."""
+    B = k.shape[0]
+    need = [-(-int(L) // P) for L in lens]
+    n_pages = sum(need) + 3
+    order = np.random.default_rng(seed).permutation(n_pages)
+    table = np.full((B, max(need + [1])), -1, dtype=np.int64)
+    kp = np.zeros((n_pages, k.shape[1], P, k.shape[3]))
+    vp = np.zeros((n_pages, v.shape[1], P, v.shape[3]))
+    nxt = 0
+    for b in range(B):
+        for blk in range(need[b]):
+            page = order[nxt]
+            nxt += 1
+            table[b, blk] = page
+            rows = slice(blk * P, min((blk + 1) * P, int(lens[b])))
+            n = rows.stop - rows.start
+            kp[page, :, :n] = k[b, :, rows]
+            vp[page, :, :n] = v[b, :, rows]
+    return kp, vp, table
+
+
+def test_paged_layout_round_trip_and_decode():
+    q, k, v, _ = _case(22, 3, 8, 2, 4, 16, 8, 150)
+    lens = np.array([150, 64, 1])
+    for P in (16, 64):
+        kp, vp, table = _to_pages(k, v, lens, P, seed=P)
+        kc, vc = oracle.paged_to_contiguous(kp, vp, table, lens, l_cap=150)
+        for b, L in enumerate(lens):
+            np.testing.assert_array_equal(kc[b, :, :L], k[b, :, :L])
+            np.testing.assert_array_equal(vc[b, :, :L], v[b, :, :L])
+            assert (kc[b, :, L:] == 0).all()
+        a, la = oracle.decode_paged(q, kp, vp, table, lens)
+        ref, lref = oracle.decode(q, k, v, lens)
+        np.testing.assert_array_equal(a, ref)
+        np.testing.assert_array_equal(la, lref)
 
 
 def test_ragged_batch_and_empty_context():
