@@ -22,6 +22,7 @@ import torch
 
 __all__ = ["DQKVError", "lib_path", "load", "decode", "decode_chunk",
            "decode_workspace_bytes", "decode_selective", "selective_workspace_bytes",
+           "decode_paged", "kv_append_paged", "kv_group_sharing",
            "prefill", "prefill_workspace_bytes", "kv_append", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +49,9 @@ SIGNATURES = {
     "diffqkv_decode_combine": (_i32, [_i32] * 9 + [_vp] * 3 + [_i32, _vp, _sz, _vp]),
     "diffqkv_decode_selective_workspace": (_i32, [_i32] * 8 + [ctypes.POINTER(_sz)]),
     "diffqkv_decode_selective": (_i32, [_i32] * 9 + [_f32, _i32] + [_vp] * 10 + [_sz, _vp]),
+    "kv_append_paged": (_i32, [_i32] * 11 + [_vp] * 7),
+    "diffqkv_decode_paged": (_i32, [_i32] * 11 + [_f32] + [_vp] * 9 + [_i32, _vp, _sz, _vp]),
+    "kv_group_sharing": (_i32, [_i32] * 8 + [_vp] * 5),
 }
 
 _lib = None
@@ -254,6 +258,84 @@ def decode_selective(q, k_cache, v_cache, ctx_len, *, top_k=100, max_ctx=None, s
         _ptr(out), _ptr(lse), _ptr(sel_idx), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse, sel_idx
+
+
+def _pages_shape(k_pages, v_pages, block_table, B=None):
+    num_pages, n_k, P, d_k = k_pages.shape
+    if v_pages.shape[0] != num_pages or v_pages.shape[2] != P:
+        raise ValueError("k_pages [N, n_k, P, d_k] and v_pages [N, n_v, P, d_v] must agree")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+            (B is not None and block_table.shape[0] != B):
+        raise ValueError("block_table must be int32 [B, max_blocks]")
+    return num_pages, n_k, P, d_k, v_pages.shape[1], v_pages.shape[3], block_table.shape[1]
+
+
+def kv_append_paged(k_new, v_new, pos, block_table, k_pages, v_pages, *, n_q=None,
+                    stream=None):
+    """kv_append into a paged cache: token t of sequence b goes to row
+    pos[b] + t, i.e. slot (row % P) of page block_table[b, row // P]."""
+    _device_tensors(k_new, v_new, pos, block_table, k_pages, v_pages)
+    B, T, n_k, d_k = k_new.shape
+    num_pages, n_k2, P, d_k2, n_v, d_v, max_blocks = _pages_shape(k_pages, v_pages,
+                                                                  block_table, B)
+    if (n_k2, d_k2) != (n_k, d_k) or v_new.shape != (B, T, n_v, d_v):
+        raise ValueError("inconsistent page / new-row shapes")
+    if pos.dtype != torch.int32 or pos.numel() != B:
+        raise ValueError("pos must be int32 [B]")
+    n_q = max(n_k, n_v) if n_q is None else n_q
+    _check("kv_append_paged", load().kv_append_paged(
+        n_q, n_k, n_v, d_k, d_v, _dtype_code(k_new), B, T, P, num_pages, max_blocks,
+        _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(block_table), _ptr(k_pages), _ptr(v_pages),
+        _stream(stream)))
+
+
+def decode_paged(q, k_pages, v_pages, block_table, ctx_len, *, max_ctx=None, scale=None,
+                 out=None, lse=None, chunk_tokens=0, workspace=None, k_new=None, v_new=None,
+                 stream=None):
+    """decode() over a paged cache (k_pages [N, n_k, P, d_k], v_pages
+    [N, n_v, P, d_v], block_table int32 [B, max_blocks])."""
+    _device_tensors(q, k_pages, v_pages, block_table, ctx_len, out, lse, workspace, k_new,
+                    v_new)
+    B, n_q, d_k = q.shape
+    num_pages, n_k, P, d_k2, n_v, d_v, max_blocks = _pages_shape(k_pages, v_pages,
+                                                                 block_table, B)
+    if d_k2 != d_k:
+        raise ValueError("q and k_pages disagree on d_k")
+    if ctx_len.dtype != torch.int32 or ctx_len.numel() != B:
+        raise ValueError("ctx_len must be int32 [B]")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    max_ctx = max_blocks * P if max_ctx is None else int(max_ctx)
+    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, n_q, d_v), dtype=q.dtype, device=q.device)
+    need = decode_workspace_bytes(n_q, n_k, n_v, d_k, d_v, B, max_ctx, chunk_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("diffqkv_decode_paged", load().diffqkv_decode_paged(
+        n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, P, num_pages, max_blocks, max_ctx, scale,
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+        _ptr(ctx_len), _ptr(out), _ptr(lse), int(chunk_tokens), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+def kv_group_sharing(k_cache, v_cache, *, n_q=None, stream=None):
+    """Expand the side with fewer heads to max(n_k, n_v) heads (each head
+    repeated in place); returns new (k, v) tensors."""
+    _device_tensors(k_cache, v_cache)
+    B, n_k, l_cap, d_k = k_cache.shape
+    n_v, d_v = v_cache.shape[1], v_cache.shape[3]
+    if v_cache.shape[0] != B or v_cache.shape[2] != l_cap or v_cache.dtype != k_cache.dtype:
+        raise ValueError("inconsistent K / V cache shapes")
+    n_h = max(n_k, n_v)
+    n_q = n_h if n_q is None else n_q
+    k_out = torch.empty((B, n_h, l_cap, d_k), dtype=k_cache.dtype, device=k_cache.device)
+    v_out = torch.empty((B, n_h, l_cap, d_v), dtype=v_cache.dtype, device=v_cache.device)
+    _check("kv_group_sharing", load().kv_group_sharing(
+        n_q, n_k, n_v, d_k, d_v, _dtype_code(k_cache), B, l_cap, _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_out), _ptr(v_out), _stream(stream)))
+    return k_out, v_out
 
 
 def prefill_workspace_bytes(n_q, n_k, n_v, d_k, d_v, batch, t_new) -> int:

@@ -431,4 +431,114 @@ int32_t diffqkv_decode_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t 
   return to_status(dqkv::launch_decode_selective(a));
 }
 
+// ---------------------------------------------------------------- paged cache
+
+// Validates a page geometry; fills *pm and the row capacity it implies.
+static int check_pages(int32_t page_rows, int32_t num_pages, int32_t max_blocks,
+                       const int32_t* table, dqkv::PageMap* pm, int* cap) {
+  if (page_rows < 64 || page_rows > (1 << 20) || (page_rows & (page_rows - 1)) != 0)
+    return DQKV_ERR_SHAPE;
+  if (num_pages < 1 || max_blocks < 1) return DQKV_ERR_SHAPE;
+  int shift = 0;
+  while ((1 << shift) < page_rows) ++shift;
+  const long long c = (long long)max_blocks * page_rows;
+  if (c > 0x7fffffffLL) return DQKV_ERR_UNSUPPORTED;
+  pm->table = table;
+  pm->max_blocks = max_blocks;
+  pm->page_shift = shift;
+  pm->num_pages = num_pages;
+  *cap = (int)c;
+  return DQKV_OK;
+}
+
+int32_t kv_append_paged(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                        int32_t dtype, int32_t batch, int32_t t_new, int32_t page_rows,
+                        int32_t num_pages, int32_t max_blocks, const void* k_new,
+                        const void* v_new, const int32_t* pos, const int32_t* block_table,
+                        void* k_pages, void* v_pages, void* stream) {
+  int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+  if (st) return st;
+  st = check_dtype_dims(dtype, d_k, d_v);
+  if (st) return st;
+  if (batch < 0 || t_new < 0 || batch > 65535) return DQKV_ERR_SHAPE;
+  dqkv::PageMap pm;
+  int cap = 0;
+  st = check_pages(page_rows, num_pages, max_blocks, block_table, &pm, &cap);
+  if (st) return st;
+  if (batch == 0 || t_new == 0) return DQKV_OK;
+  if (!k_new || !v_new || !pos || !block_table || !k_pages || !v_pages) return DQKV_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pages) || !aligned16(v_pages))
+    return DQKV_ERR_ALIGN;
+  dqkv::AppendArgs a;
+  a.elem_bytes = dtype == DQKV_BF16 ? 2 : 4;
+  a.n_k = n_k; a.n_v = n_v; a.d_k = d_k; a.d_v = d_v;
+  a.batch = batch; a.t_new = t_new; a.l_cap = cap;
+  a.k_new = k_new; a.v_new = v_new; a.pos = pos;
+  a.k_cache = k_pages; a.v_cache = v_pages;
+  a.pages = pm;
+  a.stream = (hipStream_t)stream;
+  return to_status(dqkv::launch_kv_append(a));
+}
+
+int32_t diffqkv_decode_paged(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                             int32_t dtype, int32_t batch, int32_t page_rows,
+                             int32_t num_pages, int32_t max_blocks, int32_t max_ctx,
+                             float scale, const void* q, const void* k_new, const void* v_new,
+                             void* k_pages, void* v_pages, const int32_t* block_table,
+                             const int32_t* ctx_len, void* out, float* lse,
+                             int32_t chunk_tokens, void* workspace,
+                             size_t workspace_bytes_given, void* stream) {
+  dqkv::PageMap pm;
+  int cap = 0;
+  int st = check_pages(page_rows, num_pages, max_blocks, block_table, &pm, &cap);
+  if (st) return st;
+  if (batch == 0 && n_q > 0) {
+    st = check_heads(n_q, n_k, n_v, d_k, d_v);
+    return st ? st : check_dtype_dims(dtype, d_k, d_v);
+  }
+  if ((k_new == nullptr) != (v_new == nullptr)) return DQKV_ERR_NULL;
+  if (!block_table) return DQKV_ERR_NULL;
+  dqkv::DecodeArgs a;
+  st = prepare_decode(n_q, n_k, n_v, d_k, d_v, dtype, batch, cap, max_ctx, scale, q, k_pages,
+                      v_pages, ctx_len, out, lse, chunk_tokens, workspace,
+                      workspace_bytes_given, stream, true, true, &a);
+  if (st) return st;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return DQKV_ERR_ALIGN;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.pages = pm;
+  st = to_status(dqkv::launch_decode_split(a));
+  if (st) return st;
+  return to_status(dqkv::launch_decode_combine(a));
+}
+
+// ------------------------------------------------------ kv_group_sharing
+
+int32_t kv_group_sharing(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                         int32_t dtype, int32_t batch, int32_t l_cap, const void* k_cache,
+                         const void* v_cache, void* k_out, void* v_out, void* stream) {
+  int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+  if (st) return st;
+  st = check_dtype_dims(dtype, d_k, d_v);
+  if (st) return st;
+  if (batch < 0 || l_cap < 0 || batch > 65535) return DQKV_ERR_SHAPE;
+  const int n_h = n_k > n_v ? n_k : n_v;
+  if (n_h > 65535) return DQKV_ERR_UNSUPPORTED;
+  if (batch == 0 || l_cap == 0) return DQKV_OK;
+  if (!k_cache || !v_cache || !k_out || !v_out) return DQKV_ERR_NULL;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_out) || !aligned16(v_out))
+    return DQKV_ERR_ALIGN;
+  const size_t e = dtype == DQKV_BF16 ? 2 : 4;
+  dqkv::ExpandArgs a;
+  a.batch = batch;
+  a.stream = (hipStream_t)stream;
+  a.n_src = n_k; a.n_dst = n_h; a.head_bytes = (size_t)l_cap * d_k * e;
+  a.src = k_cache; a.dst = k_out;
+  st = to_status(dqkv::launch_expand_heads(a));
+  if (st) return st;
+  a.n_src = n_v; a.n_dst = n_h; a.head_bytes = (size_t)l_cap * d_v * e;
+  a.src = v_cache; a.dst = v_out;
+  return to_status(dqkv::launch_expand_heads(a));
+}
+
 }  // extern "C"

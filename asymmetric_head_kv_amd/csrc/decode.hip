@@ -41,13 +41,18 @@ constexpr int kTile = 64;  // rows per wave iteration: one score per lane
 // H = query heads per wave.  With H = 2 the wave takes two consecutive query
 // heads that share one K head and one V head (n_q = 2 n_v): each K and V row
 // it loads serves both, halving the per-CU load traffic of such layouts.
-template <typename T, int DK, int DV, int H>
+//
+// PAGED: kc / vc are page pools and row j of sequence b sits in page
+// pm.table[b][j / page_rows] (see PageMap).  Pages hold a multiple of 64 rows
+// and chunks start at multiples of 64, so a 64-row tile never straddles two
+// pages: one table entry per tile, read one tile ahead.
+template <typename T, int DK, int DV, int H, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const T* __restrict__ q, const T* kc, const T* vc,
     const int32_t* __restrict__ ctx_len, float* __restrict__ part_ml,
     float* __restrict__ part_acc, int n_q, int n_k, int n_v, int l_cap,
     int max_ctx, int S, int C, float qscale, const T* __restrict__ k_new,
-    const T* __restrict__ v_new, T* kc_w, T* vc_w) {
+    const T* __restrict__ v_new, T* kc_w, T* vc_w, PageMap pm) {
   // kc / kc_w (and vc / vc_w) are the same cache: the kernel reads rows
   // other than the appended one through the first and writes only that row
   // through the second.
@@ -83,9 +88,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int e = 0; e < EPL; ++e) qf[hh][e] *= qscale;
   }
 
-  const T* kp = kc + (((size_t)b * n_k + hk) * l_cap + j0) * DK + kl * EPL;
   const int vl = lane % LPR_V, vr = lane / LPR_V;
-  const T* vp = vc + (((size_t)b * n_v + hv) * l_cap + j0) * DV + vl * EPL;
+  // Address of row 0 of the 64-row tile that starts at chunk row t0 (this
+  // lane's slice of it), for K and for V.
+  auto page_of = [&](int t0) -> size_t {
+    const int blk = pm.table[(size_t)b * pm.max_blocks + ((j0 + t0) >> pm.page_shift)];
+    return (size_t)min(max(blk, 0), pm.num_pages - 1);
+  };
+  auto k_tile = [&](auto* base, int t0, size_t page) {
+    if constexpr (PAGED)
+      return base + ((page * n_k + hk) * ((size_t)1 << pm.page_shift) +
+                     ((j0 + t0) & ((1 << pm.page_shift) - 1))) * DK + kl * EPL;
+    return base + (((size_t)b * n_k + hk) * l_cap + j0 + t0) * DK + kl * EPL;
+  };
+  auto v_tile = [&](auto* base, int t0, size_t page) {
+    if constexpr (PAGED)
+      return base + ((page * n_v + hv) * ((size_t)1 << pm.page_shift) +
+                     ((j0 + t0) & ((1 << pm.page_shift) - 1))) * DV + vl * EPL;
+    return base + (((size_t)b * n_v + hv) * l_cap + j0 + t0) * DV + vl * EPL;
+  };
 
   // Fused append: the sequence's newest row (L - 1) is read from k_new /
   // v_new instead of the cache, and written to the cache by one wave per
@@ -96,12 +117,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const T* kn = fused ? k_new + ((size_t)b * n_k + hk) * DK + kl * EPL : nullptr;
   const T* vn = fused ? v_new + ((size_t)b * n_v + hv) * DV + vl * EPL : nullptr;
   if (fused && r_new < rows) {
+    const int t_new0 = r_new & ~63;  // tile holding the new row
+    const size_t pg = PAGED ? page_of(t_new0) : 0;
+    const int in_tile = r_new - t_new0;
     if (i0 % (n_q / n_k) == 0 && lane < LPR_K)
-      *reinterpret_cast<u32x4*>(kc_w + (((size_t)b * n_k + hk) * l_cap + L - 1) * DK + kl * EPL) =
-          load16(kn);
+      *reinterpret_cast<u32x4*>(k_tile(kc_w, t_new0, pg) + (size_t)in_tile * DK) = load16(kn);
     if (i0 % (n_q / n_v) == 0 && lane < LPR_V)
-      *reinterpret_cast<u32x4*>(vc_w + (((size_t)b * n_v + hv) * l_cap + L - 1) * DV + vl * EPL) =
-          load16(vn);
+      *reinterpret_cast<u32x4*>(v_tile(vc_w, t_new0, pg) + (size_t)in_tile * DV) = load16(vn);
   }
 
   // The lane keeps the score of tile row my_row = kl * RPL_K + kr (K load kl,
@@ -118,25 +140,31 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
   }
 
-  auto load_k = [&](int r) -> u32x4 {
+  // r: row within the chunk; kt / vt: the tile's row-0 addresses.
+  auto load_k = [&](int r, const T* kt, int t0) -> u32x4 {
     if (r >= rows) return u32x4{0u, 0u, 0u, 0u};
-    return load16(r == r_new ? kn : kp + (size_t)r * DK);
+    return load16(r == r_new ? kn : kt + (size_t)(r - t0) * DK);
   };
-  auto load_v = [&](int r) -> u32x4 {
+  auto load_v = [&](int r, const T* vt, int t0) -> u32x4 {
     if (r >= rows) return u32x4{0u, 0u, 0u, 0u};
-    return r == r_new ? load16(vn) : load16_nt(vp + (size_t)r * DV);
+    return r == r_new ? load16(vn) : load16_nt(vt + (size_t)(r - t0) * DV);
   };
+  size_t page_next = PAGED ? page_of(0) : 0;
 
   // One tile of 64 rows per iteration: all of its K loads and the first VB
   // V loads are issued together and the scores wait only for K.  (Keeping a
   // second tile's loads in flight -- double buffers, or re-filling each
   // register right after use -- costs occupancy and measured slower.)
   for (int t0 = 0; t0 < rows; t0 += kTile) {
+    const size_t page = page_next;
+    if constexpr (PAGED) page_next = t0 + kTile < rows ? page_of(t0 + kTile) : 0;
+    const T* kt = k_tile(kc, t0, page);
+    const T* vt = v_tile(vc, t0, page);
     u32x4 kv[NK], vv[VB];
 #pragma unroll
-    for (int u = 0; u < NK; ++u) kv[u] = load_k(t0 + u * RPL_K + kr);
+    for (int u = 0; u < NK; ++u) kv[u] = load_k(t0 + u * RPL_K + kr, kt, t0);
 #pragma unroll
-    for (int u = 0; u < VB; ++u) vv[u] = load_v(t0 + u * RPL_V + vr);
+    for (int u = 0; u < VB; ++u) vv[u] = load_v(t0 + u * RPL_V + vr, vt, t0);
 
     // Scores (one row per lane per head) and the online-softmax update.
     float s_mine[H];
@@ -173,7 +201,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int vb = 0; vb < NV; vb += VB) {
       if (vb > 0) {  // only for fp32 with wide V rows: next batch of loads
 #pragma unroll
-        for (int u = 0; u < VB; ++u) vv[u] = load_v(t0 + (vb + u) * RPL_V + vr);
+        for (int u = 0; u < VB; ++u) vv[u] = load_v(t0 + (vb + u) * RPL_V + vr, vt, t0);
       }
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
@@ -298,23 +326,25 @@ static int heads_per_wave(const DecodeArgs& a) {
   return (a.n_q == 2 * a.n_v && (a.n_q / a.n_k) % 2 == 0) ? 2 : 1;
 }
 
+template <typename T, int DK, int DV, int H, bool PAGED>
+static void launch_split_hp(const DecodeArgs& a) {
+  dim3 grid(a.C, (a.n_q + 4 * H - 1) / (4 * H), a.batch);
+  hipLaunchKernelGGL((decode_split_kernel<T, DK, DV, H, PAGED>), grid, dim3(256), 0, a.stream,
+                     (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.ctx_len,
+                     a.part_ml, a.part_acc, a.n_q, a.n_k, a.n_v, a.l_cap, a.max_ctx, a.S, a.C,
+                     a.scale * kLog2e, (const T*)a.k_new, (const T*)a.v_new, (T*)a.k_cache,
+                     (T*)a.v_cache, a.pages);
+}
+
 template <typename T, int DK, int DV>
 static hipError_t launch_split_t(const DecodeArgs& a) {
-  const float qscale = a.scale * kLog2e;
-  const int H = heads_per_wave(a);
-  dim3 grid(a.C, (a.n_q + 4 * H - 1) / (4 * H), a.batch);
-  if (H == 2) {
-    hipLaunchKernelGGL((decode_split_kernel<T, DK, DV, 2>), grid, dim3(256), 0, a.stream,
-                       (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.ctx_len,
-                       a.part_ml, a.part_acc, a.n_q, a.n_k, a.n_v, a.l_cap, a.max_ctx, a.S,
-                       a.C, qscale, (const T*)a.k_new, (const T*)a.v_new, (T*)a.k_cache,
-                       (T*)a.v_cache);
+  const bool paged = a.pages.table != nullptr;
+  if (heads_per_wave(a) == 2) {
+    if (paged) launch_split_hp<T, DK, DV, 2, true>(a);
+    else launch_split_hp<T, DK, DV, 2, false>(a);
   } else {
-    hipLaunchKernelGGL((decode_split_kernel<T, DK, DV, 1>), grid, dim3(256), 0, a.stream,
-                       (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.ctx_len,
-                       a.part_ml, a.part_acc, a.n_q, a.n_k, a.n_v, a.l_cap, a.max_ctx, a.S,
-                       a.C, qscale, (const T*)a.k_new, (const T*)a.v_new, (T*)a.k_cache,
-                       (T*)a.v_cache);
+    if (paged) launch_split_hp<T, DK, DV, 1, true>(a);
+    else launch_split_hp<T, DK, DV, 1, false>(a);
   }
   return hipGetLastError();
 }

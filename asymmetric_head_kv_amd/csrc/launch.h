@@ -8,6 +8,16 @@
 
 namespace dqkv {
 
+// Paged cache: row j of sequence b lives in page table[b * max_blocks +
+// j / page_rows], slot j % page_rows; K pages [num_pages][n_k][page_rows][d_k],
+// V pages [num_pages][n_v][page_rows][d_v].  table == nullptr: contiguous.
+struct PageMap {
+  const int32_t* table = nullptr;
+  int max_blocks = 0;
+  int page_shift = 0;  // log2(page_rows); page_rows is a multiple of 64
+  int num_pages = 0;
+};
+
 struct DecodeArgs {
   bool bf16;
   int n_q, n_k, n_v, d_k, d_v;
@@ -24,6 +34,7 @@ struct DecodeArgs {
   float* part_acc;  // [B][n_q][C][d_v]
   const void* k_new;  // fused append: newest row per sequence, or null
   const void* v_new;
+  PageMap pages;
   hipStream_t stream;
 };
 
@@ -36,6 +47,19 @@ struct AppendArgs {
   const int32_t* pos;
   void* k_cache;
   void* v_cache;
+  PageMap pages;
+  hipStream_t stream;
+};
+
+// kv_group_sharing: copy of a head-major cache [B][n_src][l_cap][d] to
+// [B][n_dst][l_cap][d], destination head h reading source head
+// floor(h * n_src / n_dst).
+struct ExpandArgs {
+  int n_src, n_dst;
+  size_t head_bytes;  // l_cap * d * element size, a multiple of 16
+  int batch;
+  const void* src;
+  void* dst;
   hipStream_t stream;
 };
 
@@ -87,6 +111,7 @@ struct SelectiveArgs {
 hipError_t launch_decode_split(const DecodeArgs& a);
 hipError_t launch_decode_combine(const DecodeArgs& a);
 hipError_t launch_kv_append(const AppendArgs& a);
+hipError_t launch_expand_heads(const ExpandArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_decode_selective(const SelectiveArgs& a);
 

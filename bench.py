@@ -60,6 +60,10 @@ def parse():
     p.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     p.add_argument("--selective-k", type=int, default=100,
                    help="top_k of the selective-V decode leg (0 = skip it)")
+    p.add_argument("--page-rows", type=int, default=64,
+                   help="page size of the paged-cache leg (0 = skip it)")
+    p.add_argument("--no-compat", action="store_true",
+                   help="skip the kv_group_sharing leg")
     p.add_argument("--kernel-only", action="store_true",
                    help="only run steps (for profilers); skip twin, prefill, CPU baseline")
     p.add_argument("--ket", action="store_true",
@@ -189,6 +193,80 @@ class DecodeBench:
                               + self.B * n_q * (d_k + d_v) * self.esize      # q, out
                               + self.B * (n_k * d_k + n_v * d_v) * self.esize)  # appended rows
         self.sel_ws_traffic = 2 * n_q * int(self.ctx.sum()) * 4   # logits written, re-read
+
+    def setup_paged(self, page_rows: int, seed: int = 0):
+        """Paged copies of every cache replica: each sequence's blocks of
+        page_rows rows go to pages in a seeded random order."""
+        torch = self.torch
+        P = page_rows
+        B, cap = self.B, self.l_cap
+        nblk = -(-cap // P)
+        g = torch.Generator().manual_seed(seed)
+        perm = torch.randperm(B * nblk, generator=g)
+        inv = torch.empty_like(perm)
+        inv[perm] = torch.arange(B * nblk)
+        self.page_rows, self.max_blocks, self.num_pages = P, nblk, B * nblk
+        self.block_table = inv.view(B, nblk).to(torch.int32).to("cuda")
+
+        def to_pages(c):
+            b_, h, _, d = c.shape
+            x = torch.zeros((b_, h, nblk * P, d), dtype=c.dtype, device="cuda")
+            x[:, :, :cap] = c
+            x = x.view(b_, h, nblk, P, d).permute(0, 2, 1, 3, 4).reshape(b_ * nblk, h, P, d)
+            return x[perm.to("cuda")].contiguous()
+
+        self.pages = [(to_pages(k), to_pages(v)) for k, v in self.caches]
+
+    def paged_step(self, r):
+        """The decode step (fused append + split + combine) over paged caches."""
+        kp, vp = self.pages[r]
+        st = self.lib.diffqkv_decode_paged(
+            *self.shape, self.dtype_code, self.B, self.page_rows, self.num_pages,
+            self.max_blocks, self.max_ctx, self.case.scale, self.q.data_ptr(),
+            self.k_new.data_ptr(), self.v_new.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+            self.block_table.data_ptr(), self.ctx_t.data_ptr(), self.out.data_ptr(),
+            self.lse.data_ptr(), self.chunk, self.ws.data_ptr(), self.ws_bytes, self._stream())
+        assert st == 0, st
+
+    def setup_compat(self):
+        """kv_group_sharing copies of every replica (n_h = max(n_k, n_v) heads
+        on both sides) and the time of one expansion."""
+        torch, dq = self.torch, self.dq
+        self.compat = []
+        for k, v in self.caches:
+            self.compat.append(dq.kv_group_sharing(k, v, n_q=self.shape[0]))
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k, v = self.caches[0]
+        t0.record()
+        for _ in range(5):
+            dq.kv_group_sharing(k, v, n_q=self.shape[0])
+        t1.record()
+        torch.cuda.synchronize()
+        self.compat_expand_ms = t0.elapsed_time(t1) / 5
+        n_q, n_k, n_v, d_k, d_v = self.shape
+        n_h = max(n_k, n_v)
+        self.compat_shape = (n_q, n_h, n_h, d_k, d_v)
+        self.compat_ws_bytes = dq.decode_workspace_bytes(*self.compat_shape, self.B,
+                                                         self.max_ctx, self.chunk)
+        self.compat_ws = torch.empty(self.compat_ws_bytes, dtype=torch.uint8, device="cuda")
+        kn = self.k_new.view(self.B, n_k, d_k)
+        idx = torch.tensor([h * n_k // n_h for h in range(n_h)], device="cuda")
+        self.compat_k_new = kn[:, idx].contiguous()
+        vn = self.v_new.view(self.B, n_v, d_v)
+        idx = torch.tensor([h * n_v // n_h for h in range(n_h)], device="cuda")
+        self.compat_v_new = vn[:, idx].contiguous()
+
+    def compat_step(self, r):
+        """The decode step on the kv_group_sharing layout."""
+        k, v = self.compat[r]
+        st = self.lib.diffqkv_decode_append(
+            *self.compat_shape, self.dtype_code, self.B, self.l_cap, self.max_ctx,
+            self.case.scale, self.q.data_ptr(), self.compat_k_new.data_ptr(),
+            self.compat_v_new.data_ptr(), k.data_ptr(), v.data_ptr(), self.ctx_t.data_ptr(),
+            self.out.data_ptr(), self.lse.data_ptr(), self.chunk, self.compat_ws.data_ptr(),
+            self.compat_ws_bytes, self._stream())
+        assert st == 0, st
 
     def selective_step(self, r):
         """One decode step with selective V: append, logits, top-k, gather."""
@@ -506,6 +584,28 @@ def main():
             "workspace_bytes_per_step": bench.sel_ws_traffic,
             "speedup_over_full_decode": round(ms / ms_sel, 3),
             "step": "fused kv_append + logits + per-range top-k + final top-k and V gather"}
+    if args.page_rows > 0 and not args.kernel_only:
+        bench.setup_paged(args.page_rows)
+        ms_pg, _ = bench.time_steps(args.steps, args.warmup, args.eager, bench.paged_step)
+        log(f"paged step (page rows {args.page_rows}) {ms_pg * 1e3:.2f} us")
+        result["paged"] = {"page_rows": args.page_rows, "us_per_step": round(ms_pg * 1e3, 2),
+                           "GBps": round(bench.alg_bytes_step / (ms_pg * 1e-3) / 1e9, 1),
+                           "time_over_contiguous": round(ms_pg / ms, 3),
+                           "pages": "each sequence's blocks in a seeded random page order"}
+        bench.pages = None
+    n_q_, n_k_, n_v_, d_k_, d_v_ = bench.shape
+    if not args.no_compat and not args.kernel_only and n_k_ != n_v_:
+        bench.setup_compat()
+        ms_cp, _ = bench.time_steps(args.steps, args.warmup, args.eager, bench.compat_step)
+        n_h = max(n_k_, n_v_)
+        ratio = kv_elements_per_token(n_h, d_k_, n_h, d_v_) / kv_elements_per_token(
+            n_k_, d_k_, n_v_, d_v_)
+        log(f"kv_group_sharing step {ms_cp * 1e3:.2f} us")
+        result["kv_group_sharing"] = {
+            "heads": [n_q_, n_h, n_h], "us_per_step": round(ms_cp * 1e3, 2),
+            "time_over_native": round(ms_cp / ms, 3), "cache_bytes_ratio": round(ratio, 3),
+            "expand_us_once": round(bench.compat_expand_ms * 1e3, 1)}
+        bench.compat = None
     sym_name = None if args.no_twin else (args.twin or TWINS.get(args.workload))
     asym_bytes = bench.alg_bytes_step
     bench.free()

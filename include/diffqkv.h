@@ -258,6 +258,66 @@ int32_t diffqkv_decode_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t 
                                  int32_t* sel_idx, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * Paged cache -- a serving layout (the architecture page names vLLM's paged
+ * attention as prior art that treats K and V alike; here K and V keep
+ * separate page pools with their own row shapes under one page table):
+ *
+ *   k_pages      [num_pages][n_k][page_rows][d_k]
+ *   v_pages      [num_pages][n_v][page_rows][d_v]
+ *   block_table  [B][max_blocks] int32 (device): row j of sequence b is
+ *                slot j % page_rows of page block_table[b][j / page_rows]
+ *
+ * page_rows is a power of two >= 64 (a 64-row decode tile then never spans
+ * two pages, so each tile costs one table read).  The row capacity of a
+ * sequence is max_blocks * page_rows.  Table entries outside
+ * [0, num_pages) are not followed: kv_append_paged skips such rows and the
+ * decode reads page 0 in their place (a result for a malformed table, never
+ * an out-of-bounds access).
+ *
+ * kv_append_paged -- kv_append into a paged cache (pos, t_new, k_new, v_new
+ *   as for kv_append; rows past the capacity are skipped).
+ * diffqkv_decode_paged -- diffqkv_decode / diffqkv_decode_append over a paged
+ *   cache; k_new / v_new optional (both or neither) as for
+ *   diffqkv_decode_append; max_ctx <= max_blocks * page_rows; the workspace is
+ *   diffqkv_decode_workspace's for the same sizes.  With the same chunking
+ *   the result is bit-identical to diffqkv_decode on the gathered caches.
+ */
+int32_t kv_append_paged(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                        int32_t d_v, int32_t dtype, int32_t batch, int32_t t_new,
+                        int32_t page_rows, int32_t num_pages, int32_t max_blocks,
+                        const void* k_new, const void* v_new, const int32_t* pos,
+                        const int32_t* block_table, void* k_pages, void* v_pages,
+                        void* stream);
+
+int32_t diffqkv_decode_paged(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                             int32_t d_v, int32_t dtype, int32_t batch,
+                             int32_t page_rows, int32_t num_pages,
+                             int32_t max_blocks, int32_t max_ctx, float scale,
+                             const void* q, const void* k_new, const void* v_new,
+                             void* k_pages, void* v_pages,
+                             const int32_t* block_table, const int32_t* ctx_len,
+                             void* out, float* lse, int32_t chunk_tokens,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * kv_group_sharing -- the compatibility expansion for frameworks whose
+ * kernels need n_k = n_v (architecture page, FlexHeadFA section: the
+ * kv_group_sharing wrapper, which the page warns negates the K saving).
+ * Writes k_out [B][n_h][l_cap][d_k] and v_out [B][n_h][l_cap][d_v] with
+ * n_h = max(n_k, n_v): output head h copies input head floor(h * n_k / n_h)
+ * of K (floor(h * n_v / n_h) of V), so each head of the smaller side appears
+ * n_h / n_smaller times in a row and the larger side is copied unchanged.
+ * Decoding the expanded caches with (n_q, n_h, n_h, d_k, d_v) gives the same
+ * result as the original layout.  A bit-exact copy of all l_cap rows; the
+ * outputs must not overlap the inputs.
+ */
+int32_t kv_group_sharing(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                         int32_t d_v, int32_t dtype, int32_t batch, int32_t l_cap,
+                         const void* k_cache, const void* v_cache, void* k_out,
+                         void* v_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -203,3 +203,47 @@ def test_selective_workspace_and_validation(lib):
     assert call(q=FAKE + 4) == ALIGN and call(kn=FAKE, vn=FAKE + 2) == ALIGN
     assert call(ws_bytes=need - 1) == WS
     assert call(B=0) == OK
+
+
+def test_paged_and_compat_validation(lib):
+    def dec(**kw):
+        a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=1, P=64, N=16, MB=16,
+                 max_ctx=1024, scale=0.125, q=FAKE, kn=None, vn=None, kp=FAKE, vp=FAKE,
+                 tab=FAKE, ctx=FAKE, out=FAKE, lse=None, chunk=0, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.diffqkv_decode_paged(
+            a["n_q"], a["n_k"], a["n_v"], a["d_k"], a["d_v"], a["dtype"], a["B"], a["P"],
+            a["N"], a["MB"], a["max_ctx"], a["scale"], a["q"], a["kn"], a["vn"], a["kp"],
+            a["vp"], a["tab"], a["ctx"], a["out"], a["lse"], a["chunk"], a["ws"],
+            a["ws_bytes"], None)
+    for P in (0, 16, 32, 96, 100):
+        assert dec(P=P) == SHAPE, P          # pages: a power of two >= 64 rows
+    assert dec(N=0) == SHAPE and dec(MB=0) == SHAPE
+    assert dec(max_ctx=16 * 64 + 1) == SHAPE  # beyond max_blocks * page_rows
+    assert dec(tab=None) == NULL and dec(kn=FAKE) == NULL
+    assert dec(kp=FAKE + 8) == ALIGN
+    assert dec(n_k=3) == SHAPE
+    assert dec(ws_bytes=0) == WS
+    assert dec(B=0) == OK
+
+    def app(**kw):
+        a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=2, T=1, P=64, N=8, MB=4,
+                 kn=FAKE, vn=FAKE, pos=FAKE, tab=FAKE, kp=FAKE, vp=FAKE)
+        a.update(kw)
+        return lib.kv_append_paged(a["n_q"], a["n_k"], a["n_v"], a["d_k"], a["d_v"], a["dtype"],
+                                   a["B"], a["T"], a["P"], a["N"], a["MB"], a["kn"], a["vn"],
+                                   a["pos"], a["tab"], a["kp"], a["vp"], None)
+    assert app(P=48) == SHAPE and app(N=0) == SHAPE
+    assert app(tab=None) == NULL and app(vp=FAKE + 4) == ALIGN
+    assert app(T=0) == OK and app(d_k=40) == UNSUP
+
+    def grp(**kw):
+        a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=1, cap=256, k=FAKE,
+                 v=FAKE, ko=FAKE, vo=FAKE)
+        a.update(kw)
+        return lib.kv_group_sharing(a["n_q"], a["n_k"], a["n_v"], a["d_k"], a["d_v"],
+                                    a["dtype"], a["B"], a["cap"], a["k"], a["v"], a["ko"],
+                                    a["vo"], None)
+    assert grp(n_k=5) == SHAPE and grp(dtype=3) == UNSUP
+    assert grp(ko=None) == NULL and grp(vo=FAKE + 2) == ALIGN
+    assert grp(B=0) == OK and grp(cap=0) == OK

@@ -1,0 +1,204 @@
+"""GPU parity of the cache layouts: the kv_group_sharing expansion, and the
+paged cache (decode, fused append and kv_append through a page table).
+
+The expansion is a copy and must be bit-exact; decoding the expanded layout
+must give bit-identical results to the native one (same kernels, same rows,
+same order).  A paged decode with the same chunking must be bit-identical to
+the contiguous decode of the gathered caches, and within the usual tolerance
+of the oracle, whose paged_to_contiguous defines the layout.  Pages are
+assigned in a seeded random order, with spare pages and unused table
+entries, so any wrong table lookup shows up.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_close, assert_lse_close, ints_to_dev, raw_host, to_dev, to_host, upload
+
+pytestmark = pytest.mark.gpu
+dq = pytest.importorskip("asymmetric_head_kv_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dq.load()
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def make_pages(k, v, lens, P, seed, spare=3, extra_blocks=1):
+    """Scatter head-major caches (raw host arrays) into shuffled pages.
+    Returns (k_pages, v_pages, table); unused table entries are -1."""
+    B, n_k, cap, d_k = k.shape
+    n_v, d_v = v.shape[1], v.shape[3]
+    need = [-(-int(L) // P) for L in lens]
+    n_pages = sum(need) + spare
+    order = np.random.default_rng(seed).permutation(n_pages)
+    max_blocks = max(need + [1]) + extra_blocks
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    kp = np.zeros((n_pages, n_k, P, d_k), dtype=k.dtype)
+    vp = np.zeros((n_pages, n_v, P, d_v), dtype=v.dtype)
+    nxt = 0
+    for b in range(B):
+        for blk in range(need[b]):
+            page = int(order[nxt])
+            nxt += 1
+            table[b, blk] = page
+            r0, r1 = blk * P, min((blk + 1) * P, cap)
+            kp[page, :, :r1 - r0] = k[b, :, r0:r1]
+            vp[page, :, :r1 - r0] = v[b, :, r0:r1]
+    return kp, vp, table
+
+
+# ------------------------------------------------------------ kv_group_sharing
+
+@pytest.mark.parametrize("dtype,heads", [("bf16", (16, 4, 16)), ("f32", (8, 8, 2)),
+                                         ("bf16", (32, 4, 16))])
+def test_kv_group_sharing_bit_exact_and_decode_unchanged(dtype, heads):
+    n_q, n_k, n_v = heads
+    case = synth.make_case(401, dtype=dtype, batch=2, n_q=n_q, n_k=n_k, n_v=n_v, d_k=64,
+                           d_v=128 if dtype == "bf16" else 64, ctx_len=[700, 300], l_cap=704)
+    _say("kv_group_sharing", dtype, heads)
+    q, k, v, ctx = upload(case)
+    kx, vx = dq.kv_group_sharing(k, v, n_q=n_q)
+    torch.cuda.synchronize()
+    ek, ev = oracle.kv_group_sharing(case.k_cache, case.v_cache)
+    np.testing.assert_array_equal(raw_host(kx), ek)
+    np.testing.assert_array_equal(raw_host(vx), ev)
+    lse_a = torch.empty((2, n_q), dtype=torch.float32, device="cuda")
+    lse_b = torch.empty_like(lse_a)
+    out_a, _ = dq.decode(q, k, v, ctx, scale=case.scale, lse=lse_a)
+    out_b, _ = dq.decode(q, kx, vx, ctx, scale=case.scale, lse=lse_b)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(raw_host(out_a), raw_host(out_b))
+    np.testing.assert_array_equal(lse_a.cpu().numpy(), lse_b.cpu().numpy())
+
+
+# ------------------------------------------------------------------ paged cache
+
+PAGED = [
+    # dtype, n_q, n_k, n_v, d_k, d_v, lengths, page rows
+    ("bf16", 16, 4, 16, 64, 128, [5000, 777, 64, 1], 64),
+    ("bf16", 32, 4, 16, 64, 64, [3000, 2049], 128),
+    ("bf16", 16, 16, 16, 128, 128, [1500], 256),
+    ("f32", 8, 2, 4, 64, 32, [900, 65, 129], 64),
+]
+
+
+def run_paged(case, P, seed, k_new=None, v_new=None, chunk=0):
+    kp, vp, table = make_pages(case.k_cache, case.v_cache, case.ctx_len, P, seed)
+    kp_d, vp_d = to_dev(kp, case.dtype), to_dev(vp, case.dtype)
+    tab = ints_to_dev(table)
+    q = to_dev(case.q, case.dtype)
+    ctx = ints_to_dev(case.ctx_len)
+    lse = torch.empty((case.batch, case.n_q), dtype=torch.float32, device="cuda")
+    out, _ = dq.decode_paged(q, kp_d, vp_d, tab, ctx, max_ctx=case.l_cap, scale=case.scale,
+                             lse=lse, chunk_tokens=chunk, k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    return out, lse, (kp_d, vp_d, table)
+
+
+@pytest.mark.parametrize("cfg", PAGED, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-P{c[7]}")
+def test_paged_decode_matches_contiguous_and_oracle(cfg):
+    dtype, n_q, n_k, n_v, d_k, d_v, lens, P = cfg
+    cap = max(lens)
+    case = synth.make_case(402, dtype=dtype, batch=len(lens), n_q=n_q, n_k=n_k, n_v=n_v,
+                           d_k=d_k, d_v=d_v, ctx_len=lens, l_cap=cap)
+    _say("paged decode", cfg)
+    for chunk in (0, 192):
+        out_p, lse_p, _ = run_paged(case, P, seed=P + chunk, chunk=chunk)
+        q, k, v, ctx = upload(case)
+        lse_c = torch.empty_like(lse_p)
+        out_c, _ = dq.decode(q, k, v, ctx, scale=case.scale, lse=lse_c, chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(raw_host(out_p), raw_host(out_c))
+        np.testing.assert_array_equal(lse_p.cpu().numpy(), lse_c.cpu().numpy())
+    qw, kw, vw = case.widened()
+    ref, ref_lse = oracle.decode(qw, kw, vw, case.ctx_len, case.scale)
+    err = assert_close(to_host(out_p), ref, dtype, f"paged {cfg}")
+    assert_lse_close(to_host(lse_p), ref_lse, dtype, f"paged {cfg}")
+    _say(f"  normwise rel err {err:.2e}")
+
+
+def test_paged_fused_append_matches_separate_append():
+    lens = [3001, 128, 1]
+    case = synth.make_case(403, dtype="bf16", batch=3, n_q=16, n_k=4, n_v=16, d_k=64, d_v=128,
+                           ctx_len=lens, l_cap=3072)
+    kn, vn = synth.new_rows(403, dtype="bf16", batch=3, t_new=1, n_k=4, n_v=16, d_k=64, d_v=128)
+    kn_d, vn_d = to_dev(kn, "bf16"), to_dev(vn, "bf16")
+    _say("paged fused append")
+    out_f, lse_f, (kp_f, vp_f, table) = run_paged(case, 64, seed=7, k_new=kn_d, v_new=vn_d)
+    kp, vp, _ = make_pages(case.k_cache, case.v_cache, case.ctx_len, 64, seed=7)
+    kp_s, vp_s = to_dev(kp, "bf16"), to_dev(vp, "bf16")
+    tab = ints_to_dev(table)
+    dq.kv_append_paged(kn_d, vn_d, ints_to_dev(np.asarray(lens) - 1), tab, kp_s, vp_s, n_q=16)
+    lse_s = torch.empty_like(lse_f)
+    out_s, _ = dq.decode_paged(to_dev(case.q, "bf16"), kp_s, vp_s, tab,
+                               ints_to_dev(case.ctx_len), max_ctx=3072, scale=case.scale,
+                               lse=lse_s)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(raw_host(kp_f), raw_host(kp_s))
+    np.testing.assert_array_equal(raw_host(vp_f), raw_host(vp_s))
+    np.testing.assert_array_equal(raw_host(out_f), raw_host(out_s))
+    np.testing.assert_array_equal(lse_f.cpu().numpy(), lse_s.cpu().numpy())
+    # And the appended rows are where the layout says.
+    kc, vc = oracle.paged_to_contiguous(raw_host(kp_f), raw_host(vp_f), table, case.ctx_len,
+                                        l_cap=3072)
+    for b, L in enumerate(lens):
+        np.testing.assert_array_equal(kc[b, :, L - 1], kn[b, 0])
+        np.testing.assert_array_equal(vc[b, :, L - 1], vn[b, 0])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kv_append_paged_against_oracle(dtype):
+    B, T, n_k, n_v, d_k, d_v, P = 3, 70, 2, 8, 64, 64, 64
+    lens = np.array([200, 64, 0])          # rows already cached
+    cap = 320
+    case = synth.make_case(404, dtype=dtype, batch=B, n_q=8, n_k=n_k, n_v=n_v, d_k=d_k,
+                           d_v=d_v, ctx_len=lens + T, l_cap=cap)
+    kn, vn = synth.new_rows(404, dtype=dtype, batch=B, t_new=T, n_k=n_k, n_v=n_v, d_k=d_k,
+                            d_v=d_v)
+    kp, vp, table = make_pages(case.k_cache, case.v_cache, lens + T, P, seed=11)
+    kp_d, vp_d = to_dev(kp, dtype), to_dev(vp, dtype)
+    _say("kv_append_paged", dtype)
+    dq.kv_append_paged(to_dev(kn, dtype), to_dev(vn, dtype), ints_to_dev(lens),
+                       ints_to_dev(table), kp_d, vp_d, n_q=8)
+    torch.cuda.synchronize()
+    got_k, got_v = oracle.paged_to_contiguous(raw_host(kp_d), raw_host(vp_d), table, lens + T,
+                                              l_cap=cap)
+    want_k, want_v = oracle.kv_append(case.k_cache, case.v_cache, kn, vn, lens)
+    for b in range(B):
+        L = int(lens[b]) + T
+        np.testing.assert_array_equal(got_k[b, :, :L].view(np.uint8), want_k[b, :, :L].view(np.uint8))
+        np.testing.assert_array_equal(got_v[b, :, :L].view(np.uint8), want_v[b, :, :L].view(np.uint8))
+    # Pages no sequence uses are untouched.
+    used = set(int(x) for x in table.ravel() if x >= 0)
+    for page in set(range(kp.shape[0])) - used:
+        np.testing.assert_array_equal(raw_host(kp_d)[page], kp[page])
+
+
+@pytest.mark.parametrize("P", [64, 256])
+def test_paged_full_workload(P):
+    case = synth.make_case(**synth.workload("decode32k_asym"))
+    _say("paged full workload decode32k_asym, page rows", P)
+    out_p, lse_p, _ = run_paged(case, P, seed=P)
+    q, k, v, ctx = upload(case)
+    lse_c = torch.empty_like(lse_p)
+    out_c, _ = dq.decode(q, k, v, ctx, scale=case.scale, lse=lse_c)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(raw_host(out_p), raw_host(out_c))
+    qw, kw, vw = case.widened()
+    ref, ref_lse = oracle.decode(qw, kw, vw, case.ctx_len, case.scale)
+    err = assert_close(to_host(out_p), ref, "bf16", "paged 32k")
+    assert_lse_close(to_host(lse_p), ref_lse, "bf16", "paged 32k")
+    _say(f"  normwise rel err {err:.2e}")
