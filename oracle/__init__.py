@@ -8,6 +8,8 @@ from .attention import (attend_one, attend_selective_one, attention_weights, dec
                         decode_paged, decode_selective, default_scale, group_sharing_index,
                         kv_append, kv_group_sharing, paged_to_contiguous, prefill, top_k_rows)
 
-__all__ = ["attend_one", "attend_selective_one", "attention_weights", "decode",
+from .augq import augq, silu
+
+__all__ = ["augq", "silu", "attend_one", "attend_selective_one", "attention_weights", "decode",
            "decode_paged", "decode_selective", "default_scale", "group_sharing_index",
            "kv_append", "kv_group_sharing", "paged_to_contiguous", "prefill", "top_k_rows"]

@@ -23,6 +23,7 @@ import numpy as np
 
 # Stream ids: one per tensor role.
 S_Q, S_K, S_V, S_KNEW, S_VNEW, S_LEN, S_OUTLIER = 1, 2, 3, 4, 5, 6, 7
+S_H, S_WGATE, S_WUP, S_WDOWN = 8, 9, 10, 11
 
 BF16_NAN = np.uint16(0x7FC0)
 _BLOCK = 1 << 24  # elements generated per block, bounds host memory
@@ -179,6 +180,44 @@ def new_rows(seed: int, *, dtype: str, batch: int, t_new: int, n_k: int,
     k_new = normal(seed, S_KNEW, (batch, t_new, n_k, d_k), dtype)
     v_new = normal(seed, S_VNEW, (batch, t_new, n_v, d_v), dtype)
     return k_new, v_new
+
+
+@dataclass
+class AugQCase:
+    """Inputs of the augmented-Q projection: hidden states h [M][d_m] and
+    weights in (out, in) layout, W_gate / W_up [d_i][d_m], W_down
+    [d_out][d_i]; float32 arrays or uint16 bf16 bits."""
+
+    dtype: str
+    h: np.ndarray
+    w_gate: np.ndarray
+    w_up: np.ndarray
+    w_down: np.ndarray
+
+    def widened(self):
+        if self.dtype == "f32":
+            return self.h, self.w_gate, self.w_up, self.w_down
+        return tuple(bf16_bits_to_f32(x) for x in (self.h, self.w_gate, self.w_up, self.w_down))
+
+
+def _scaled(seed, stream, shape, fan_in, dtype):
+    x = normal(seed, stream, shape, "f32") * np.float32(1.0 / math.sqrt(fan_in))
+    return x if dtype == "f32" else f32_to_bf16_bits(x)
+
+
+def make_augq(seed: int, *, M: int, d_m: int, d_i: int, d_out: int,
+              dtype: str = "bf16") -> AugQCase:
+    """Seeded augmented-Q inputs: h ~ N(0, 1); weights ~ N(0, 1/fan_in), the
+    usual initialisation scale, so the intermediate and output stay O(1)."""
+    h = normal(seed, S_H, (M, d_m), dtype)
+    return AugQCase(dtype, h, _scaled(seed, S_WGATE, (d_i, d_m), d_m, dtype),
+                    _scaled(seed, S_WUP, (d_i, d_m), d_m, dtype),
+                    _scaled(seed, S_WDOWN, (d_out, d_i), d_i, dtype))
+
+
+# The SIGMA-1.5B augmented-Q shape (architecture page, Table 14): hidden
+# 2048, augmented intermediate 3072, 32 query heads of 64 dimensions.
+AUGQ_SIGMA15B = dict(d_m=2048, d_i=3072, d_out=32 * 64)
 
 
 # ---------------------------------------------------------------------------
