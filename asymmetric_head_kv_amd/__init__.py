@@ -22,7 +22,7 @@ import torch
 
 __all__ = ["DQKVError", "lib_path", "load", "decode", "decode_chunk",
            "decode_workspace_bytes", "decode_selective", "selective_workspace_bytes",
-           "decode_paged", "kv_append_paged", "kv_group_sharing",
+           "decode_paged", "kv_append_paged", "kv_group_sharing", "augq", "augq_pack",
            "prefill", "prefill_workspace_bytes", "kv_append", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,6 +52,9 @@ SIGNATURES = {
     "kv_append_paged": (_i32, [_i32] * 11 + [_vp] * 7),
     "diffqkv_decode_paged": (_i32, [_i32] * 11 + [_f32] + [_vp] * 9 + [_i32, _vp, _sz, _vp]),
     "kv_group_sharing": (_i32, [_i32] * 8 + [_vp] * 5),
+    "augq_workspace": (_i32, [_i32] * 4 + [ctypes.POINTER(_sz)]),
+    "augq_forward": (_i32, [_i32] * 4 + [_vp] * 6 + [_sz, _vp]),
+    "augq_pack": (_i32, [_i32] * 2 + [_vp] * 3),
 }
 
 _lib = None
@@ -336,6 +339,44 @@ def kv_group_sharing(k_cache, v_cache, *, n_q=None, stream=None):
         n_q, n_k, n_v, d_k, d_v, _dtype_code(k_cache), B, l_cap, _ptr(k_cache), _ptr(v_cache),
         _ptr(k_out), _ptr(v_out), _stream(stream)))
     return k_out, v_out
+
+
+def augq_pack(w, *, stream=None):
+    """Pack a bf16 weight [n_out, n_in] (out, in layout) for augq: returns
+    [n_out // 16, n_in // 32, 64, 8] in matrix-core fragment order."""
+    _device_tensors(w)
+    if w.dtype != torch.bfloat16 or w.dim() != 2:
+        raise TypeError("augq_pack takes a 2-D bfloat16 weight")
+    n_out, n_in = w.shape
+    wp = torch.empty((n_out // 16, n_in // 32, 64, 8), dtype=torch.bfloat16, device=w.device)
+    _check("augq_pack", load().augq_pack(n_out, n_in, _ptr(w), _ptr(wp), _stream(stream)))
+    return wp
+
+
+def augq(h, w_gate_p, w_up_p, w_down_p, *, out=None, workspace=None, stream=None):
+    """Augmented-Q projection, bf16: q = (silu(h W_gate^T) * h W_up^T) W_down^T.
+    h [M, d_m]; weights packed by augq_pack (w_gate, w_up from [d_i, d_m],
+    w_down from [d_out, d_i]).  Returns q [M, d_out]."""
+    _device_tensors(h, w_gate_p, w_up_p, w_down_p, out, workspace)
+    M, d_m = h.shape
+    d_i = w_gate_p.shape[0] * 16
+    d_out = w_down_p.shape[0] * 16
+    for w, n_out, n_in in ((w_gate_p, d_i, d_m), (w_up_p, d_i, d_m), (w_down_p, d_out, d_i)):
+        if tuple(w.shape) != (n_out // 16, n_in // 32, 64, 8):
+            raise ValueError("weights must come from augq_pack with matching sizes")
+    for t in (h, w_gate_p, w_up_p, w_down_p):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("augq takes bfloat16 tensors")
+    if out is None:
+        out = torch.empty((M, d_out), dtype=torch.bfloat16, device=h.device)
+    need = _sz()
+    _check("augq_workspace", load().augq_workspace(M, d_m, d_i, d_out, ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 16), dtype=torch.uint8, device=h.device)
+    _check("augq_forward", load().augq_forward(
+        M, d_m, d_i, d_out, _ptr(h), _ptr(w_gate_p), _ptr(w_up_p), _ptr(w_down_p), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
 
 
 def prefill_workspace_bytes(n_q, n_k, n_v, d_k, d_v, batch, t_new) -> int:

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdiffqkv.so")
 
-SOURCES = ["api.hip", "kv_append.hip", "decode.hip", "prefill.hip", "selective.hip"]
+SOURCES = ["api.hip", "kv_append.hip", "decode.hip", "prefill.hip", "selective.hip", "augq.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -541,4 +541,45 @@ int32_t kv_group_sharing(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int
   return to_status(dqkv::launch_expand_heads(a));
 }
 
+// ------------------------------------------------------- augmented Q
+
+int32_t augq_workspace(int32_t M, int32_t d_m, int32_t d_i, int32_t d_out, size_t* bytes) {
+  if (!bytes) return DQKV_ERR_NULL;
+  if (M < 0 || d_m <= 0 || d_i <= 0 || d_out <= 0) return DQKV_ERR_SHAPE;
+  *bytes = (size_t)M * d_i * 2;
+  return DQKV_OK;
+}
+
+int32_t augq_forward(int32_t M, int32_t d_m, int32_t d_i, int32_t d_out, const void* h,
+                     const void* w_gate, const void* w_up, const void* w_down, void* q,
+                     void* workspace, size_t workspace_bytes_given, void* stream) {
+  if (M < 0 || d_m <= 0 || d_i <= 0 || d_out <= 0) return DQKV_ERR_SHAPE;
+  // Reductions split up to sixteen ways in 32-wide steps; outputs in
+  // 16-column tiles.
+  if (d_m % 1024 != 0 || d_i % 1024 != 0 || d_i % 16 != 0 || d_out % 16 != 0)
+    return DQKV_ERR_UNSUPPORTED;
+  if ((long long)d_i / 16 > 0x7fffffffLL || (M + 15) / 16 > 65535) return DQKV_ERR_UNSUPPORTED;
+  if (M == 0) return DQKV_OK;
+  if (!h || !w_gate || !w_up || !w_down || !q || !workspace) return DQKV_ERR_NULL;
+  if (!aligned16(h) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(workspace))
+    return DQKV_ERR_ALIGN;
+  if (workspace_bytes_given < (size_t)M * d_i * 2) return DQKV_ERR_WORKSPACE;
+  dqkv::AugQArgs a;
+  a.M = M; a.d_m = d_m; a.d_i = d_i; a.d_out = d_out;
+  a.h = h; a.w_gate = w_gate; a.w_up = w_up; a.w_down = w_down;
+  a.act = workspace; a.q = q;
+  a.stream = (hipStream_t)stream;
+  return to_status(dqkv::launch_augq(a));
+}
+
+int32_t augq_pack(int32_t n_out, int32_t n_in, const void* w, void* w_packed, void* stream) {
+  if (n_out < 0 || n_in < 0) return DQKV_ERR_SHAPE;
+  if (n_out % 16 != 0 || n_in % 32 != 0) return DQKV_ERR_UNSUPPORTED;
+  if (n_out == 0 || n_in == 0) return DQKV_OK;
+  if (!w || !w_packed) return DQKV_ERR_NULL;
+  if (!aligned16(w) || !aligned16(w_packed)) return DQKV_ERR_ALIGN;
+  return to_status(dqkv::launch_augq_pack(w, w_packed, n_out, n_in, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -108,11 +108,27 @@ struct SelectiveArgs {
   hipStream_t stream;
 };
 
+// Augmented-Q projection (bf16): h [M][d_m]; w_gate, w_up [d_i][d_m];
+// w_down [d_out][d_i], all three packed (launch_augq_pack); act [M][d_i]
+// (the gated intermediate); q [M][d_out].
+struct AugQArgs {
+  int M, d_m, d_i, d_out;
+  const void* h;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  void* act;
+  void* q;
+  hipStream_t stream;
+};
+
 hipError_t launch_decode_split(const DecodeArgs& a);
 hipError_t launch_decode_combine(const DecodeArgs& a);
 hipError_t launch_kv_append(const AppendArgs& a);
 hipError_t launch_expand_heads(const ExpandArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 hipError_t launch_decode_selective(const SelectiveArgs& a);
+hipError_t launch_augq(const AugQArgs& a);
+hipError_t launch_augq_pack(const void* w, void* wp, int N, int K, hipStream_t stream);
 
 }  // namespace dqkv

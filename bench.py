@@ -64,6 +64,7 @@ def parse():
                    help="page size of the paged-cache leg (0 = skip it)")
     p.add_argument("--no-compat", action="store_true",
                    help="skip the kv_group_sharing leg")
+    p.add_argument("--no-augq", action="store_true", help="skip the augmented-Q leg")
     p.add_argument("--kernel-only", action="store_true",
                    help="only run steps (for profilers); skip twin, prefill, CPU baseline")
     p.add_argument("--ket", action="store_true",
@@ -462,6 +463,78 @@ def prefill_bench(steps: int = 10):
             "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
 
 
+def augq_bench(steps: int = 200):
+    """The augmented-Q projection at the SIGMA-1.5B shape for 1 and 16 decode
+    tokens (weight streaming; per-layer weight replicas so the timing is HBM,
+    not the Infinity Cache) and for 2048 prefill tokens (matrix cores)."""
+    import numpy as np
+    import torch
+
+    import asymmetric_head_kv_amd as dq
+    import synth
+
+    sh = synth.AUGQ_SIGMA15B
+    d_m, d_i, d_out = sh["d_m"], sh["d_i"], sh["d_out"]
+    case = synth.make_augq(7, M=2048, **sh)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+            torch.bfloat16).to("cuda")
+
+    w = [dq.augq_pack(up(x)) for x in (case.w_gate, case.w_up, case.w_down)]
+    wbytes = sum(x.numel() for x in w) * 2
+    R = max(2, math.ceil(4 * MALL_BYTES / wbytes))
+    reps = [w] + [[x.clone() for x in w] for _ in range(R - 1)]
+    h_all = up(case.h)
+    lib = dq.load()
+    out = {"shape": {"d_m": d_m, "d_i": d_i, "d_out": d_out}, "weight_bytes": wbytes,
+           "weight_replicas": R}
+    for M in (1, 16, 2048):
+        h = h_all[:M].contiguous()
+        q = torch.empty((M, d_out), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(16, M * d_i * 2), dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def call(r):
+            wg, wu, wd = reps[r]
+            st = lib.augq_forward(M, d_m, d_i, d_out, h.data_ptr(), wg.data_ptr(), wu.data_ptr(),
+                                  wd.data_ptr(), q.data_ptr(), ws.data_ptr(),
+                                  ws.numel(), torch.cuda.current_stream().cuda_stream)
+            assert st == 0, st
+
+        for r in range(R):
+            call(r)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            call(0)
+        torch.cuda.current_stream().wait_stream(s)
+        with torch.cuda.graph(g):
+            for r in range(R):
+                call(r)
+        g.replay()
+        torch.cuda.synchronize()
+        n = max(1, (steps if M < 2048 else 20) // R)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(n):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / (n * R) * 1e3
+        flops = 2 * M * (2 * d_m * d_i + d_i * d_out)
+        byts = wbytes + 2 * M * (d_m + 2 * d_i + d_out)
+        out[f"M{M}"] = {"us": round(us, 2), "GBps": round(byts / us / 1e3, 1),
+                        "frac_hbm": round(byts / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "tflops": round(flops / us / 1e6, 1),
+                        "frac_mfma": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4)}
+        log(f"augq M={M}: {us:.2f} us")
+        del g
+    return out
+
+
 def hbm_copy_gbs(nbytes: int = 2 << 30, reps: int = 10):
     """Practical HBM ceiling: a large device-to-device copy (read + write)."""
     import torch
@@ -629,6 +702,9 @@ def main():
         if not args.no_prefill:
             log("prefill 2048 on 30720")
             result["prefill"] = prefill_bench()
+        if not args.no_augq:
+            log("augmented Q")
+            result["augq"] = augq_bench()
         if not args.no_cpu_baseline:
             log("cpu baseline (oracle)")
             result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)

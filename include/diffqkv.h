@@ -318,6 +318,40 @@ int32_t kv_group_sharing(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
                          const void* k_cache, const void* v_cache, void* k_out,
                          void* v_out, void* stream);
 
+/*
+ * augq_forward -- the augmented-Q projection (architecture page, section 3.2
+ * item 4: Augmented Q with SwiGLU gating), bf16 in and out, fp32
+ * accumulation:
+ *
+ *   a = silu(h W_gate^T) * (h W_up^T)   [M][d_i], rounded to bf16 (workspace)
+ *   q = a W_down^T                       [M][d_out]
+ *
+ * h [M][d_m] (M tokens); weights given PACKED by augq_pack from the (out,
+ * in) layout: w_gate, w_up from [d_i][d_m], w_down from [d_out][d_i]
+ * (d_i = 3072, d_m = 2048, d_out = n_q * d_k = 2048 for SIGMA-1.5B).  For
+ * decode, q [M][d_out] is the query tensor [B][n_q][d_k] that diffqkv_decode
+ * takes.  d_m and d_i multiples of 1024, d_out a multiple of 16.  workspace:
+ * augq_workspace bytes (M * d_i bf16), 16-byte aligned.  Two kernels on
+ * `stream`.
+ *
+ * augq_pack -- one-time weight layout change for augq_forward: w [n_out][n_in]
+ * (bf16, row-major) -> w_packed [n_out / 16][n_in / 32][64][8], element
+ * (nb, kb, l, e) = w[16 nb + l % 16][32 kb + 8 (l / 16) + e]: the operand
+ * order of the matrix-core instruction, so each 1 KiB fragment is read in one
+ * contiguous wave load.  n_out a multiple of 16, n_in of 32; w_packed holds
+ * n_out * n_in elements and must not overlap w.
+ */
+int32_t augq_pack(int32_t n_out, int32_t n_in, const void* w, void* w_packed,
+                  void* stream);
+
+int32_t augq_workspace(int32_t M, int32_t d_m, int32_t d_i, int32_t d_out,
+                       size_t* bytes);
+
+int32_t augq_forward(int32_t M, int32_t d_m, int32_t d_i, int32_t d_out,
+                     const void* h, const void* w_gate, const void* w_up,
+                     const void* w_down, void* q, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

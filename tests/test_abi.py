@@ -247,3 +247,25 @@ def test_paged_and_compat_validation(lib):
     assert grp(n_k=5) == SHAPE and grp(dtype=3) == UNSUP
     assert grp(ko=None) == NULL and grp(vo=FAKE + 2) == ALIGN
     assert grp(B=0) == OK and grp(cap=0) == OK
+
+
+def test_augq_validation(lib):
+    def call(**kw):
+        a = dict(M=4, d_m=2048, d_i=3072, d_out=2048, h=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, q=FAKE,
+                 ws=FAKE, ws_bytes=4 * 3072 * 2)
+        a.update(kw)
+        return lib.augq_forward(a["M"], a["d_m"], a["d_i"], a["d_out"], a["h"], a["wg"], a["wu"],
+                                a["wd"], a["q"], a["ws"], a["ws_bytes"], None)
+    assert call(M=-1) == SHAPE and call(d_out=0) == SHAPE
+    assert call(d_m=1000) == UNSUP and call(d_i=3000) == UNSUP and call(d_out=100) == UNSUP
+    assert call(wd=None) == NULL and call(h=FAKE + 2) == ALIGN
+    assert call(ws_bytes=4 * 3072 * 2 - 1) == WS
+    assert call(M=0) == OK
+    size = ctypes.c_size_t()
+    assert lib.augq_workspace(7, 2048, 3072, 2048, ctypes.byref(size)) == OK
+    assert size.value == 7 * 3072 * 2
+    assert lib.augq_pack(24, 64, FAKE, FAKE, None) == UNSUP      # n_out % 16
+    assert lib.augq_pack(32, 48, FAKE, FAKE, None) == UNSUP      # n_in % 32
+    assert lib.augq_pack(32, 64, None, FAKE, None) == NULL
+    assert lib.augq_pack(32, 64, FAKE, FAKE + 8, None) == ALIGN
+    assert lib.augq_pack(0, 64, None, None, None) == OK
