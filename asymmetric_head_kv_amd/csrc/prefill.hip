@@ -8,11 +8,12 @@
 //
 // Work split: a workgroup = 4 waves = 128 consecutive query rows of one query
 // head; each wave owns 32 rows.  The workgroup walks the visible keys in
-// tiles of 64, double-buffered in LDS: the K tile row-major (rows padded by
-// 16 bytes against bank conflicts) and the V tile rearranged so that every
-// lane's 8 matrix-core operands for one value column are 16 contiguous
-// bytes.  Everything is computed transposed so that each lane owns one query
-// row:
+// tiles of 64, double-buffered in LDS.  Tiles travel from HBM straight into
+// LDS (16-byte global_load_lds, no register staging): K and V row-major, their
+// 16-byte slots XOR-swizzled by row against bank conflicts.  The V^T operand
+// is read with ds_read_b64_tr_b16, which hands each lane one value column for
+// four consecutive keys, so V needs no rearranging.  Everything is computed
+// transposed so that each lane owns one query row:
 //   S^T[key][q]  = K . Q^T   (v_mfma_f32_32x32x16_bf16: A = K from LDS,
 //                             B = Q^T held in registers for the whole walk)
 //   P^T          = 2^(S^T * scale * log2 e - m), online max / sum per lane
@@ -24,8 +25,8 @@
 //                             S^T accumulators, rounded to bf16)
 // In the 32x32 accumulator layout lane l holds column l % 32 and rows
 // 8*(r/4) + 4*(l/32) + r%4 for register r; the keys a lane holds for a
-// 16-key step are therefore {4h..4h+3, 8+4h..8+4h+3} (h = l/32), and the V
-// tile is stored with exactly that key order so that A and B agree.
+// 16-key step are therefore {4h..4h+3, 8+4h..8+4h+3} (h = l/32), and the two
+// transposed V reads of an operand fetch exactly those two key quads.
 //
 // Workgroups are renumbered so that the q-tiles of a head, and the heads of
 // a K group, are dispatched to the same XCD and share its L2.
@@ -39,28 +40,38 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kPfWaves = 4;
 constexpr int kPfRowsPerWave = 32;
 constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // query rows per workgroup
 constexpr int kPfKeys = 64;                          // keys per tile
 
+// LDS tile layout: rows of 16-byte slots; logical slot c of key row j sits at
+// physical slot c ^ swizzle(j).  The gfx950 LDS serves 256 bytes (64 banks)
+// per cycle: a 16-byte read serves 16 lanes at a time, an 8-byte read 32, and
+// lanes served together conflict when their addresses meet modulo 256 bytes
+// (measured with the bank-conflict counter).  K is read 16 bytes per lane,
+// 16 consecutive key rows per cycle at one logical slot: the swizzle spreads
+// them over the 16 slots of a 256-byte window.  V is read 8 bytes per lane
+// (transposed), 4 key rows x 4 logical slots per cycle: the swizzle moves
+// each of the 4 rows to its own group of 4 slots.
 template <int DK, int DV>
 struct PfLds {
-  static constexpr int kPitch = DK * 2 + 16;               // K row pitch (bytes)
-  static constexpr int kKBytes = kPfKeys * kPitch;
+  static constexpr int K16 = DK / 8;                 // 16-byte slots per K row
+  static constexpr int V16 = DV / 8;                 // per V row
+  static constexpr int KR256 = 16 / K16;             // K rows per 256 bytes
+  static constexpr int VR256 = 16 / V16;             // V rows per 256 bytes
+  static constexpr int kKBytes = kPfKeys * DK * 2;
   static constexpr int kVBytes = kPfKeys * DV * 2;
   static constexpr int kStage = kKBytes + kVBytes;
   static constexpr int kTotal = 2 * kStage;
+  __device__ static int kswz(int j) { return (j / KR256) & (K16 - 1); }
+  __device__ static int vswz(int j) { return 4 * ((j / VR256) & (V16 / 4 - 1)); }
 };
-
-// V tile in LDS: for 16-key step s, lane half h and value column d, the 16
-// bytes at slot (s * 2 + h) * d_v + vswz(d) hold that column's 8 keys of the
-// half, so the 32 lanes of a half read one contiguous run (no bank
-// conflicts).  vswz XORs a column's low three bits with bits 3-5: each group
-// of 8 columns stays in place for the reads while the cooperative stores,
-// whose lanes are 8 columns apart, spread over the banks.
-__device__ __forceinline__ int vswz(int d) { return d ^ ((d >> 3) & 7); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
@@ -79,10 +90,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   using Lds = PfLds<DK, DV>;
   constexpr int KS = DK / 16;       // 16-wide d_k steps of S^T
   constexpr int NB = DV / 32;       // 32-wide d_v blocks of O^T
-  constexpr int K16 = DK / 8;       // 16-byte chunks per K row
-  constexpr int KCH = kPfKeys * K16 / 256;  // K chunks per thread per tile
-  constexpr int VD8 = DV / 8;       // 8-column chunks per V row
-  static_assert(KCH >= 1, "K tile");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   // Renumber workgroups: linear id -> (head, key split, q-tile) so that
@@ -129,81 +136,65 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const bf16* kbase = kc + ((size_t)b * n_k + hk) * l_cap * DK;
   const bf16* vbase = vc + ((size_t)b * n_v + hv) * l_cap * DV;
 
-  // Cooperative tile loads.  K: KCH 16-byte chunks per thread.  V: each
-  // thread owns 4 consecutive keys x 8 consecutive columns.
-  const int v_dc = tid % VD8;            // column chunk
-  const int v_kq = tid / VD8;            // key quad (0..15 when active)
-  const bool v_act = VD8 * (kPfKeys / 4) >= 256 || v_kq < kPfKeys / 4;
-  u32x4 kreg[KCH];
-  u32x4 vreg[4];
-
-  // Per-thread base pointers of the cooperative loads; a tile adds j0 rows.
-  // Rows past n_keys (only in the last tile) are clamped to the last
-  // visible row: the loads stay in bounds and every score they feed is
-  // masked.
-  const bf16* kthr[KCH];
+  // Tile loads, HBM -> LDS: per round the workgroup's 256 lanes fill 256
+  // consecutive 16-byte slots (wave w: slots 64w .. 64w+63, in lane order).
+  // Lane-constant parts: the key row of this lane's slot and the element
+  // offset of its logical chunk within the row.
+  constexpr int KR = kPfKeys * Lds::K16 / 256;   // K rounds per tile
+  constexpr int VR = kPfKeys * Lds::V16 / 256;   // V rounds per tile
+  static_assert(KR >= 1 && VR >= 1, "tile");
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int k_row[KR], k_off[KR], v_row[VR], v_off[VR];
 #pragma unroll
-  for (int c = 0; c < KCH; ++c) {
-    const int e = tid + c * 256;
-    kthr[c] = kbase + (size_t)(e / K16) * DK + (e % K16) * 8;
+  for (int r = 0; r < KR; ++r) {
+    const int slot = r * 256 + tid;
+    k_row[r] = slot / Lds::K16;
+    k_off[r] = ((slot % Lds::K16) ^ Lds::kswz(k_row[r])) * 8;
   }
-  const bf16* vthr = vbase + (size_t)(v_kq * 4) * DV + v_dc * 8;
-  auto load_tile = [&](int t) {
+#pragma unroll
+  for (int r = 0; r < VR; ++r) {
+    const int slot = r * 256 + tid;
+    v_row[r] = slot / Lds::V16;
+    v_off[r] = ((slot % Lds::V16) ^ Lds::vswz(v_row[r])) * 8;
+  }
+  // Rows past n_keys (only in the last tile) are clamped to the last visible
+  // row: the loads stay in bounds and every score they feed is masked.
+  auto issue_tile = [&](int t, int stage) {
     const int j0 = t * kPfKeys;
-    if (j0 + kPfKeys <= n_keys) {
+    unsigned char* kl = lds + stage * Lds::kStage + wave_u * 1024;
+    unsigned char* vl = lds + stage * Lds::kStage + Lds::kKBytes + wave_u * 1024;
+    const bool full = j0 + kPfKeys <= n_keys;
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) kreg[c] = load16(kthr[c] + (size_t)j0 * DK);
-      if (v_act) {
+    for (int r = 0; r < KR; ++r) {
+      const int j = full ? j0 + k_row[r] : min(j0 + k_row[r], n_keys - 1);
+      __builtin_amdgcn_global_load_lds(kbase + (uint32_t)(j * DK + k_off[r]),
+                                       (lds_void*)(kl + r * 4096), 16, 0, 0);
+    }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) vreg[k] = load16(vthr + (size_t)(j0 + k) * DV);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < KCH; ++c) {
-        const int e = tid + c * 256;
-        const int j = min(j0 + e / K16, n_keys - 1);
-        kreg[c] = load16(kbase + (size_t)j * DK + (e % K16) * 8);
-      }
-      if (v_act) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int j = min(j0 + v_kq * 4 + k, n_keys - 1);
-          vreg[k] = load16(vbase + (size_t)j * DV + v_dc * 8);
-        }
-      }
+    for (int r = 0; r < VR; ++r) {
+      const int j = full ? j0 + v_row[r] : min(j0 + v_row[r], n_keys - 1);
+      __builtin_amdgcn_global_load_lds(vbase + (uint32_t)(j * DV + v_off[r]),
+                                       (lds_void*)(vl + r * 4096), 16, 0, 0);
     }
   };
 
-  auto store_tile = [&](int stage) {
-    unsigned char* kl = lds + stage * Lds::kStage;
-    unsigned char* vl = kl + Lds::kKBytes;
+  // Operand addresses within a stage (bytes).  K (A of S^T, 16 bytes): key
+  // row kb * 32 + col, logical slot 2 ks + h.
+  int k_rd[KS];
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int e = tid + c * 256;
-      const int key = e / K16, ch = e % K16;
-      *reinterpret_cast<u32x4*>(kl + key * Lds::kPitch + ch * 16) = kreg[c];
-    }
-    if (v_act) {
-      // Keys 4*v_kq .. +3 lie in 16-key step s = v_kq / 4, quad qq = v_kq % 4:
-      // quads 0,1 fill bytes 0-7 of halves h = 0,1; quads 2,3 bytes 8-15.
-      const int s = v_kq >> 2, qq = v_kq & 3;
-      const int hh = qq & 1, off = (qq >> 1) * 8;
-      // Transpose the 4 keys x 8 columns block: column d gets 4 keys (8 bytes).
-#pragma unroll
-      for (int dw = 0; dw < 4; ++dw) {       // word dw holds columns 2dw, 2dw+1
-        const uint32_t w0 = vreg[0][dw], w1 = vreg[1][dw], w2 = vreg[2][dw], w3 = vreg[3][dw];
-        // low halves (column 2dw) of keys 0..3, then high halves (column 2dw+1)
-        const uint32_t lo01 = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
-        const int d0 = v_dc * 8 + 2 * dw;
-        uint2* p0 = reinterpret_cast<uint2*>(vl + ((s * 2 + hh) * DV + vswz(d0)) * 16 + off);
-        uint2* p1 = reinterpret_cast<uint2*>(vl + ((s * 2 + hh) * DV + vswz(d0 + 1)) * 16 + off);
-        *p0 = make_uint2(lo01, lo23);
-        *p1 = make_uint2(hi01, hi23);
-      }
-    }
+  for (int ks = 0; ks < KS; ++ks)
+    k_rd[ks] = (col * Lds::K16 + ((2 * ks + h) ^ Lds::kswz(col))) * 16;
+  // V^T (A of O^T), two transposed 8-byte reads per operand: in 16-lane
+  // group g, lane j points at key row 16 st + 4 (g / 2) + j / 4 (+ 8 for the
+  // second read) and value columns 32 n + 16 (g % 2) + 4 (j % 4) .. +3; lane i
+  // of the group then holds column 32 n + 16 (g % 2) + i for the four rows.
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int v_key = 4 * (g16 >> 1) + (j16 >> 2);          // + 16 st (+ 8)
+  const int v_col = 16 * (g16 & 1) + 4 * (j16 & 3);        // + 32 n
+  auto v_rd = [&](int st, int n, int second) -> int {
+    const int key = 16 * st + v_key + 8 * second;
+    const int d = 32 * n + v_col;
+    return (key * Lds::V16 + ((d >> 3) ^ Lds::vswz(key))) * 16 + (d & 7) * 2;
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -211,56 +202,33 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
   for (int n = 0; n < NB; ++n) o[n] = f32x16{};
 
-  if (t_begin < t_end) {
-    load_tile(t_begin);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = t_begin; t < t_end; ++t) {
-    const int stage = (t - t_begin) & 1;
-    load_tile(t + 1);  // past the last tile: clamped rows, stored but never read
-    const unsigned char* kl = lds + stage * Lds::kStage;
-    const unsigned char* vl = kl + Lds::kKBytes;
-    const int j0 = t * kPfKeys;
-
-    // S^T for two 32-key blocks.
-    f32x16 s[2];
+  const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+  // S^T of one tile (K in LDS at kl) into sx: two 32-key blocks.
+  auto qk = [&](const unsigned char* kl, f32x16 (&sx)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+      sx[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            kl + (kb * 32 + col) * Lds::kPitch + (ks * 16 + 8 * h) * 2));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s[kb], 0, 0, 0);
+            kl + kb * 32 * Lds::K16 * 16 + k_rd[ks]));
+        sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sx[kb], 0, 0, 0);
       }
     }
-
-    // Causal mask (only on tiles that reach past this wave's first row):
-    // key j is visible to this row iff j <= p_q.
-    const bool diag = j0 + kPfKeys - 1 > base + r0 + wave * kPfRowsPerWave;
-    if (diag) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + kb * 32 + (r >> 2) * 8 + 4 * h + (r & 3);
-          s[kb][r] = j <= p_q ? s[kb][r] : -INFINITY;
-        }
-      }
-    }
+  };
+  // Running max from a tile's scores (valid = false: the tile does not
+  // count).  Lazy rescaling: the running max only moves (and O, l are
+  // rescaled) when some row's max grows by more than 2^8; otherwise the
+  // stale max is kept, probabilities stay <= 256, and O / l is unchanged.
+  auto prep = [&](const f32x16 (&sx)[2], bool valid) {
     float smax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) smax = fmaxf(fmaxf(smax, s[kb][r]), s[kb][r + 1]);
+      for (int r = 0; r < 16; r += 2) smax = fmaxf(fmaxf(smax, sx[kb][r]), sx[kb][r + 1]);
     }
     smax = fmaxf(smax, __shfl_xor(smax, 32));
-    // Lazy rescaling: the running max only moves (and O, l are rescaled)
-    // when some row's max grows by more than 2^8; otherwise the stale max is
-    // kept, probabilities stay <= 256, and the final O / l is unchanged.
-    const float m_tile = smax * qscale;
+    const float m_tile = valid ? smax * qscale : -INFINITY;
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.f) != 0) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
@@ -269,58 +237,83 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       for (int n = 0; n < NB; ++n) o[n] *= alpha;
       m_run = m_new;
     }
+  };
+  // P for one 32-key block: exponentials, row sums, bf16 operands.
+  auto make_p = [&](const f32x16 (&sx)[2], int kb, bf16x8 (&pb)[4], float& psum,
+                    float m_use) {
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = fast_exp2(fmaf(sx[kb][r], qscale, -m_use));
+      const float p1 = fast_exp2(fmaf(sx[kb][r + 1], qscale, -m_use));
+      const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+      if constexpr (kExactSum) psum += p0 + p1;
+      else psum = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnes, psum, false);
+      pb[kb * 2 + (r >> 3)][r & 7] = pk[0];
+      pb[kb * 2 + (r >> 3)][(r & 7) + 1] = pk[1];
+    }
+  };
+  // O^T += V^T P^T for one 16-key step (V in LDS at vl).
+  auto pv = [&](const unsigned char* vl, int st, const bf16x8 (&pb)[4]) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vl + v_rd(st, n, 0)));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vl + v_rd(st, n, 1)));
+      const bf16x8 a = __builtin_bit_cast(
+          bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[n], 0, 0, 0);
+    }
+  };
+  auto stage_k = [&](int st) -> const unsigned char* { return lds + st * Lds::kStage; };
+  auto stage_v = [&](int st) -> const unsigned char* {
+    return lds + st * Lds::kStage + Lds::kKBytes;
+  };
+
+  // Two LDS stages: tile t is consumed while tile t + 1 arrives.
+  if (t_begin < t_end) issue_tile(t_begin, 0);
+  f32x16 sa[2];
+  for (int t = t_begin; t < t_end; ++t) {
+    const int sc = (t - t_begin) & 1;
+    // Tile t has landed for every wave, and every wave is done with tile
+    // t - 1, whose stage now receives tile t + 1.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < t_end) issue_tile(t + 1, sc ^ 1);
+    const int j0 = t * kPfKeys;
+    qk(stage_k(sc), sa);
+    // Causal mask (only on tiles that reach past this wave's first row): key
+    // j is visible to this row iff j <= p_q.
+    if (j0 + kPfKeys - 1 > base + r0 + wave * kPfRowsPerWave) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + kb * 32 + (r >> 2) * 8 + 4 * h + (r & 3);
+          sa[kb][r] = j <= p_q ? sa[kb][r] : -INFINITY;
+        }
+      }
+    }
+    prep(sa, true);
     const float m_use = m_run == -INFINITY ? 0.f : m_run;  // rows with nothing visible yet
     float psum = 0.f;
-    const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
     bf16x8 pb[4];
-    // P for one 32-key block: exponentials, row sums, bf16 operands.
-    auto make_p = [&](int kb) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(fmaf(s[kb][r], qscale, -m_use));
-        const float p1 = fast_exp2(fmaf(s[kb][r + 1], qscale, -m_use));
-        const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-        if constexpr (kExactSum) psum += p0 + p1;
-        else psum = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnes, psum, false);
-        pb[kb * 2 + (r >> 3)][r & 7] = pk[0];
-        pb[kb * 2 + (r >> 3)][(r & 7) + 1] = pk[1];
-      }
-    };
-    // O^T += V^T P^T for one 16-key step.
-    auto pv = [&](int st) {
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            vl + ((st * 2 + h) * DV + vswz(n * 32 + col)) * 16));
-        o[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[n], 0, 0, 0);
-      }
-    };
-    // Software overlap inside the tile: the matrix products of keys 0-31
-    // run while the VALU computes P for keys 32-63, and those of keys 32-63
-    // while it rearranges the next tile into LDS.
-    make_p(0);
-    pv(0);
-    pv(1);
-    make_p(1);
+    // Software overlap inside the tile: the matrix products of keys 0-31 run
+    // while the VALU computes P for keys 32-63.
+    make_p(sa, 0, pb, psum, m_use);
+    pv(stage_v(sc), 0, pb);
+    pv(stage_v(sc), 1, pb);
+    make_p(sa, 1, pb, psum, m_use);
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
     }
     psum += __shfl_xor(psum, 32);
     l_run += psum;
-    pv(2);
-    pv(3);
-    store_tile(stage ^ 1);  // the last tile stores a clamped copy no one reads
-#pragma unroll
-    for (int k = 0; k < 2 * NB; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-    }
-    __syncthreads();
+    pv(stage_v(sc), 2, pb);
+    pv(stage_v(sc), 3, pb);
   }
 
   // Store this lane's query row: rows 8*(r/4)+4h+r%4 of each 32-column block
