@@ -323,7 +323,23 @@ class DecodeBench:
                 fn(s % R)
         t1.record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / steps, bool(graphs)
+        ms = t0.elapsed_time(t1) / steps
+        # Spread: each replay of R steps timed alone (untimed above), per-step
+        # median and 10th / 90th percentiles.
+        self.step_pct_us = None
+        if graphs and R in graphs:
+            n = max(10, min(100, steps // R))
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+            ev[0].record()
+            for k in range(n):
+                graphs[R].replay()
+                ev[k + 1].record()
+            torch.cuda.synchronize()
+            per = sorted(ev[k].elapsed_time(ev[k + 1]) * 1e3 / R for k in range(n))
+            pick = lambda f: round(per[min(n - 1, int(f * (n - 1) + 0.5))], 2)
+            self.step_pct_us = {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9),
+                                "replays": n, "steps_per_replay": R}
+        return ms, bool(graphs)
 
     def _graph(self, fn, n):
         torch = self.torch
@@ -629,6 +645,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "us_per_step": round(ms * 1e3, 2), "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "us_per_step_spread": bench.step_pct_us,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": bench.case.dtype, "data": "synthetic",
         "config": {"workload": args.workload, "batch": bench.B, "max_ctx": bench.max_ctx,
