@@ -216,11 +216,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       }
     }
   };
-  // Running max from a tile's scores (valid = false: the tile does not
-  // count).  Lazy rescaling: the running max only moves (and O, l are
-  // rescaled) when some row's max grows by more than 2^8; otherwise the
-  // stale max is kept, probabilities stay <= 256, and O / l is unchanged.
-  auto prep = [&](const f32x16 (&sx)[2], bool valid) {
+  // Running max from a tile's scores.  Lazy rescaling: the running max only
+  // moves (and O, l are rescaled) when some row's max grows by more than
+  // 2^8; otherwise the stale max is kept, probabilities stay <= 256, and
+  // O / l is unchanged.
+  auto prep = [&](const f32x16 (&sx)[2]) {
     float smax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       for (int r = 0; r < 16; r += 2) smax = fmaxf(fmaxf(smax, sx[kb][r]), sx[kb][r + 1]);
     }
     smax = fmaxf(smax, __shfl_xor(smax, 32));
-    const float m_tile = valid ? smax * qscale : -INFINITY;
+    const float m_tile = smax * qscale;
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.f) != 0) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         }
       }
     }
-    prep(sa, true);
+    prep(sa);
     const float m_use = m_run == -INFINITY ? 0.f : m_run;  // rows with nothing visible yet
     float psum = 0.f;
     bf16x8 pb[4];
