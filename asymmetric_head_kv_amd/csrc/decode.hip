@@ -15,21 +15,25 @@
 //   * all K and V loads of the tile are issued at once (16-byte lane loads,
 //     1 KiB contiguous per wave instruction);
 //   * scores: each lane multiplies its 16-byte slice of a K row with the
-//     matching slice of q, DPP sums over the lanes of a row; each lane keeps
-//     the score of exactly one row of the tile;
+//     matching slice of q (bf16: packed two-element dot products), DPP sums
+//     over the lanes of a row; each lane keeps the score of exactly one row
+//     of the tile;
 //   * online softmax over tiles (running max m, running sum l, rescaled
 //     accumulator), max / sum by wave reductions, base-2 exponentials with
 //     log2(e) folded into the query scale;
 //   * V rows are accumulated in fp32 with each lane owning a 16-byte column
 //     slice; the row's probability arrives by ds_bpermute from the lane that
-//     owns it.
+//     owns it (bf16: two rows per step, their probabilities packed as a bf16
+//     pair and each column's two values paired by v_perm, then one packed
+//     dot product per column).
 // The chunk's (m, l, acc[d_v]) goes to the workspace.
 //
-// Combine kernel: one workgroup per (sequence, query head) merges the chunks
+// Combine kernel: one workgroup per (query head, sequence, 32 value columns)
+// merges the chunks
 //   M = max_c m_c, w_c = 2^(m_c - M), Lambda = sum_c w_c l_c,
 //   o = sum_c w_c acc_c / Lambda, lse = (M + log2 Lambda) ln 2,
-// which is exact in real arithmetic.  Chunks past the sequence's length are
-// never read.
+// which is exact in real arithmetic.  Chunks past the sequence's length never
+// enter the sums.
 
 #include "device_common.h"
 #include "launch.h"
@@ -65,6 +69,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   constexpr int NV = kTile / RPL_V;          // V wave loads per tile
   constexpr int VB = NV < 16 ? NV : 16;      // V loads held in registers at once
   static_assert(LPR_K >= 1 && LPR_K <= 32 && LPR_V >= 1 && LPR_V <= 64, "head dim");
+  // bf16: scores and the V accumulation use packed two-element dot products
+  // (v_dot2_f32_bf16, fp32 accumulation), the latter over pairs of rows
+  // RPL_V apart, with the probabilities rounded to bf16.
+  constexpr bool kDot = sizeof(T) == 2;
+  static_assert(VB % 2 == 0, "V loads are consumed in pairs");
 
   const int c = blockIdx.x, quad = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -78,14 +87,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int hk = (i0 * n_k) / n_q;        // shared by the wave's H heads
   const int hv = (i0 * n_v) / n_q;
 
-  // This lane's slice of q for each head (scaled by scale * log2 e).
+  // This lane's slice of q for each head: fp32 scaled by scale * log2 e, or
+  // for bf16 the raw pairs (the scale is applied to the finished dot).
   const int kl = lane % LPR_K, kr = lane / LPR_K;
   float qf[H][EPL];
+  u32x4 qp[H];
 #pragma unroll
   for (int hh = 0; hh < H; ++hh) {
-    Elem<T>::unpack(load16(q + ((size_t)b * n_q + i0 + hh) * DK + kl * EPL), qf[hh]);
+    qp[hh] = load16(q + ((size_t)b * n_q + i0 + hh) * DK + kl * EPL);
+    if constexpr (!kDot) {
+      Elem<T>::unpack(qp[hh], qf[hh]);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[hh][e] *= qscale;
+      for (int e = 0; e < EPL; ++e) qf[hh][e] *= qscale;
+    }
   }
 
   const int vl = lane % LPR_V, vr = lane / LPR_V;
@@ -108,22 +122,23 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     return base + (((size_t)b * n_v + hv) * l_cap + j0 + t0) * DV + vl * EPL;
   };
 
-  // Fused append: the sequence's newest row (L - 1) is read from k_new /
-  // v_new instead of the cache, and written to the cache by one wave per
-  // K head (the one holding the group's first query head) and per V head.
-  // Only this chunk touches row L - 1.
-  const bool fused = k_new != nullptr;
-  const int r_new = fused ? L - 1 - j0 : -1;  // in [0, rows) iff this chunk owns it
-  const T* kn = fused ? k_new + ((size_t)b * n_k + hk) * DK + kl * EPL : nullptr;
-  const T* vn = fused ? v_new + ((size_t)b * n_v + hv) * DV + vl * EPL : nullptr;
-  if (fused && r_new < rows) {
+  // Fused append: the sequence's newest row (L - 1) is the last row of the
+  // chunk that owns it.  Every wave of that chunk stores the row of its own K
+  // head and V head into the cache (waves sharing a head store identical
+  // bytes), waits for its stores to complete, and then reads the row back
+  // like any other.  Only this chunk touches row L - 1.
+  if (k_new != nullptr && L - 1 - j0 < rows) {
+    const int r_new = L - 1 - j0;
     const int t_new0 = r_new & ~63;  // tile holding the new row
     const size_t pg = PAGED ? page_of(t_new0) : 0;
     const int in_tile = r_new - t_new0;
-    if (i0 % (n_q / n_k) == 0 && lane < LPR_K)
-      *reinterpret_cast<u32x4*>(k_tile(kc_w, t_new0, pg) + (size_t)in_tile * DK) = load16(kn);
-    if (i0 % (n_q / n_v) == 0 && lane < LPR_V)
-      *reinterpret_cast<u32x4*>(v_tile(vc_w, t_new0, pg) + (size_t)in_tile * DV) = load16(vn);
+    if (lane < LPR_K)
+      *reinterpret_cast<u32x4*>(k_tile(kc_w, t_new0, pg) + (size_t)in_tile * DK) =
+          load16(k_new + ((size_t)b * n_k + hk) * DK + kl * EPL);
+    if (lane < LPR_V)
+      *reinterpret_cast<u32x4*>(v_tile(vc_w, t_new0, pg) + (size_t)in_tile * DV) =
+          load16(v_new + ((size_t)b * n_v + hv) * DV + vl * EPL);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // s_waitcnt on the stores
   }
 
   // The lane keeps the score of tile row my_row = kl * RPL_K + kr (K load kl,
@@ -140,14 +155,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
   }
 
-  // r: row within the chunk; kt / vt: the tile's row-0 addresses.
+  // r: row within the chunk; kt / vt: the tile's row-0 addresses.  Loads of
+  // the chunk's last tile: rows past the chunk's end read as zeros.  Every
+  // other tile takes plain loads at constant offsets from the tile's address.
   auto load_k = [&](int r, const T* kt, int t0) -> u32x4 {
     if (r >= rows) return u32x4{0u, 0u, 0u, 0u};
-    return load16(r == r_new ? kn : kt + (size_t)(r - t0) * DK);
+    return load16(kt + (size_t)(r - t0) * DK);
   };
   auto load_v = [&](int r, const T* vt, int t0) -> u32x4 {
     if (r >= rows) return u32x4{0u, 0u, 0u, 0u};
-    return r == r_new ? load16(vn) : load16_nt(vt + (size_t)(r - t0) * DV);
+    return load16_nt(vt + (size_t)(r - t0) * DV);
   };
   size_t page_next = PAGED ? page_of(0) : 0;
 
@@ -161,10 +178,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const T* kt = k_tile(kc, t0, page);
     const T* vt = v_tile(vc, t0, page);
     u32x4 kv[NK], vv[VB];
+    if (t0 + kTile <= rows) {
 #pragma unroll
-    for (int u = 0; u < NK; ++u) kv[u] = load_k(t0 + u * RPL_K + kr, kt, t0);
+      for (int u = 0; u < NK; ++u) kv[u] = load16(kt + (size_t)(u * RPL_K + kr) * DK);
 #pragma unroll
-    for (int u = 0; u < VB; ++u) vv[u] = load_v(t0 + u * RPL_V + vr, vt, t0);
+      for (int u = 0; u < VB; ++u) vv[u] = load16_nt(vt + (size_t)(u * RPL_V + vr) * DV);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NK; ++u) kv[u] = load_k(t0 + u * RPL_K + kr, kt, t0);
+#pragma unroll
+      for (int u = 0; u < VB; ++u) vv[u] = load_v(t0 + u * RPL_V + vr, vt, t0);
+    }
 
     // Scores (one row per lane per head) and the online-softmax update.
     float s_mine[H];
@@ -173,15 +197,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       float kf[EPL];
-      Elem<T>::unpack(kv[u], kf);
+      if constexpr (!kDot) Elem<T>::unpack(kv[u], kf);
 #pragma unroll
       for (int hh = 0; hh < H; ++hh) {
         float s = 0.f;
+        if constexpr (kDot) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s = fmaf(qf[hh][e], kf[e], s);
+          for (int w = 0; w < 4; ++w) s = dot2_bf16(kv[u][w], qp[hh][w], s);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) s = fmaf(qf[hh][e], kf[e], s);
+        }
         s = group_sum<LPR_K>(s);
         s_mine[hh] = (u == kl) ? s : s_mine[hh];
       }
+    }
+    if constexpr (kDot) {
+#pragma unroll
+      for (int hh = 0; hh < H; ++hh) s_mine[hh] *= qscale;
     }
     float p[H];
 #pragma unroll
@@ -196,6 +229,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
     }
 
+    // bf16: pack this lane's probability with that of row my_row ^ RPL_V
+    // (row my_row + RPL_V where my_row % (2 RPL_V) < RPL_V, the only lanes
+    // whose pair is used).
+    uint32_t pp[H];
+    if constexpr (kDot) {
+      const int partner = my_row ^ RPL_V;
+      const int psrc = (partner % RPL_K) * LPR_K + partner / RPL_K;
+#pragma unroll
+      for (int hh = 0; hh < H; ++hh) pp[hh] = pack_bf16x2(p[hh], __shfl(p[hh], psrc));
+    }
+
     // acc_h += p_h(row) * V_row for every head of the wave.
 #pragma unroll
     for (int vb = 0; vb < NV; vb += VB) {
@@ -203,17 +247,40 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
         for (int u = 0; u < VB; ++u) vv[u] = load_v(t0 + (vb + u) * RPL_V + vr, vt, t0);
       }
+      if constexpr (kDot) {
+        // Loads u and u + 1 hold rows r and r + RPL_V of the same columns;
+        // the lane owning row r holds (p[r], p[r + RPL_V]) packed in pp.
 #pragma unroll
-      for (int u = 0; u < VB; ++u) {
-        const int r = (vb + u) * RPL_V + vr;  // row within the tile
-        const int src = (r % RPL_K) * LPR_K + r / RPL_K;
-        float vf[EPL];
-        Elem<T>::unpack(vv[u], vf);
+        for (int u = 0; u < VB; u += 2) {
+          const int r = (vb + u) * RPL_V + vr;
+          const int src = (r % RPL_K) * LPR_K + r / RPL_K;
+          uint32_t pr[H];
 #pragma unroll
-        for (int hh = 0; hh < H; ++hh) {
-          const float pr = __shfl(p[hh], src);
+          for (int hh = 0; hh < H; ++hh) pr[hh] = (uint32_t)__shfl((int)pp[hh], src);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pr, vf[e], acc[hh][e]);
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = __builtin_amdgcn_perm(vv[u + 1][w], vv[u][w], 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(vv[u + 1][w], vv[u][w], 0x07060302u);
+#pragma unroll
+            for (int hh = 0; hh < H; ++hh) {
+              acc[hh][2 * w] = dot2_bf16(lo, pr[hh], acc[hh][2 * w]);
+              acc[hh][2 * w + 1] = dot2_bf16(hi, pr[hh], acc[hh][2 * w + 1]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < VB; ++u) {
+          const int r = (vb + u) * RPL_V + vr;  // row within the tile
+          const int src = (r % RPL_K) * LPR_K + r / RPL_K;
+          float vf[EPL];
+          Elem<T>::unpack(vv[u], vf);
+#pragma unroll
+          for (int hh = 0; hh < H; ++hh) {
+            const float pr = __shfl(p[hh], src);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pr, vf[e], acc[hh][e]);
+          }
         }
       }
     }
@@ -245,9 +312,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 constexpr int kCombineThreads = 256;
 constexpr int kCombineCols = 32;  // value columns per combine workgroup
 
-// One workgroup per (query head, sequence, 32-column slice of d_v).  Every
-// partial the workgroup needs is requested before any is used, so the merge
-// costs one memory round trip; the (m, l) pairs are re-read by each slice.
+// One workgroup per (query head, sequence, 32-column slice of d_v).  The
+// partial slots are requested together with the sequence length (all C
+// slots of the head exist in the workspace; those past the sequence's
+// chunk count are loaded but never used), so the merge costs one memory
+// round trip.  Each thread merges its own partials around its local max;
+// after one barrier wave 0 merges the threads' results with the same
+// rescaling, lane shuffles doing the cross-thread steps.
 template <typename T, int DV>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_acc,
@@ -256,59 +327,91 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
   constexpr int COLS = DV < kCombineCols ? DV : kCombineCols;
   constexpr int LPR = COLS / 4;               // lanes per partial row slice (float4)
   constexpr int CPP = kCombineThreads / LPR;  // partials per pass
-  constexpr int U = 4;                        // passes whose loads are in flight together
-  __shared__ float red[kCombineThreads / 64];
+  constexpr int G = 64 / LPR;                 // partial groups per wave-0 lane column
+  constexpr int U = 4;                        // passes loaded up front
+  static_assert(CPP % G == 0, "combine shape");
   __shared__ f32x4 part[CPP][LPR];
+  __shared__ float pm[CPP], pl[CPP];
 
   const int i = blockIdx.x, b = blockIdx.y, slice = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int L = ctx_len[b];
-  L = max(0, min(L, min(max_ctx, l_cap)));
-  const int nc = min(C, (L + S - 1) / S);
-  const size_t base = ((size_t)b * n_q + i) * C;
+  const int tid = threadIdx.x;
   const int cl = tid % LPR, cr = tid / LPR;
+  const size_t base = ((size_t)b * n_q + i) * C;
   const float* src = part_acc + base * DV + slice * COLS + cl * 4;
 
-  // Issue the first U passes of partial loads and this thread's (m, l).
+  const int L_raw = ctx_len[b];
   f32x4 a[U];
-  float mc[U];
+  float mc[U], lc[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int c = cr + u * CPP;
-    a[u] = c < nc ? *reinterpret_cast<const f32x4*>(src + (size_t)c * DV) : f32x4{0.f, 0.f, 0.f, 0.f};
-    mc[u] = c < nc ? part_ml[2 * (base + c)] : -INFINITY;
+    if (c < C) {
+      a[u] = *reinterpret_cast<const f32x4*>(src + (size_t)c * DV);
+      mc[u] = part_ml[2 * (base + c)];
+      lc[u] = part_ml[2 * (base + c) + 1];
+    }
   }
-  // Global max over all chunks.
-  float M = -INFINITY;
-  for (int c = tid; c < nc; c += kCombineThreads) M = fmaxf(M, part_ml[2 * (base + c)]);
-  M = wave_max(M);
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  // Denominator Lambda = sum_c 2^(m_c - M) l_c.
-  float lam = 0.f;
-  for (int c = tid; c < nc; c += kCombineThreads)
-    lam += fast_exp2(part_ml[2 * (base + c)] - M) * part_ml[2 * (base + c) + 1];
-  lam = wave_sum(lam);
-  if (lane == 0) red[wave] = lam;
+  const int L = max(0, min(L_raw, min(max_ctx, l_cap)));
+  const int nc = min(C, (L + S - 1) / S);
 
+  // This thread's partials c = cr, cr + CPP, ... below nc.
+  float m_t = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (cr + u * CPP < nc) m_t = fmaxf(m_t, mc[u]);
+  for (int c = cr + U * CPP; c < nc; c += CPP) m_t = fmaxf(m_t, part_ml[2 * (base + c)]);
+  float l_t = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const float w = cr + u * CPP < nc ? fast_exp2(mc[u] - M) : 0.f;
-    o += w * a[u];
+    if (cr + u * CPP < nc) {
+      const float w = fast_exp2(mc[u] - m_t);
+      l_t += w * lc[u];
+      o += w * a[u];
+    }
   }
-  for (int c = cr + U * CPP; c < nc; c += CPP)
-    o += fast_exp2(part_ml[2 * (base + c)] - M) * *reinterpret_cast<const f32x4*>(src + (size_t)c * DV);
+  for (int c = cr + U * CPP; c < nc; c += CPP) {
+    const float w = fast_exp2(part_ml[2 * (base + c)] - m_t);
+    l_t += w * part_ml[2 * (base + c) + 1];
+    o += w * *reinterpret_cast<const f32x4*>(src + (size_t)c * DV);
+  }
   part[cr][cl] = o;
+  if (cl == 0) {
+    pm[cr] = m_t;
+    pl[cr] = l_t;
+  }
   __syncthreads();
-  lam = red[0] + red[1] + red[2] + red[3];
-  if (tid < LPR) {
-    f32x4 t = part[0][tid];
-    for (int k = 1; k < CPP; ++k) t += part[k][tid];
+  if (tid >= 64) return;
+
+  // Wave 0: lane = g * LPR + col; group g takes thread rows g, g + G, ...
+  const int col = tid % LPR, g = tid / LPR;
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = g; k < CPP; k += G) M = fmaxf(M, pm[k]);
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  f32x4 t = {0.f, 0.f, 0.f, 0.f};
+  float lam = 0.f;
+#pragma unroll
+  for (int k = g; k < CPP; k += G) {
+    const float mk = pm[k];
+    if (mk > -INFINITY) {  // rows with no partial hold (-inf, 0, 0)
+      const float w = fast_exp2(mk - M);
+      t += w * part[k][col];
+      lam += w * pl[k];
+    }
+  }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    t.x += __shfl_xor(t.x, off);
+    t.y += __shfl_xor(t.y, off);
+    t.z += __shfl_xor(t.z, off);
+    t.w += __shfl_xor(t.w, off);
+    lam += __shfl_xor(lam, off);
+  }
+  if (g == 0) {
     const float inv = nc > 0 ? 1.f / lam : 0.f;
-    T* dst = out + ((size_t)b * n_q + i) * DV + slice * COLS + tid * 4;
+    T* dst = out + ((size_t)b * n_q + i) * DV + slice * COLS + col * 4;
     dst[0] = Elem<T>::from_f32(t.x * inv);
     dst[1] = Elem<T>::from_f32(t.y * inv);
     dst[2] = Elem<T>::from_f32(t.z * inv);
