@@ -12,15 +12,17 @@
 // contiguous memory (eight full cache lines) instead of 64-byte pieces of
 // sixteen rows, which is what lets the weight stream reach HBM speed.
 //
-// One kernel template, C[M][N] = A[M][K] . B[N][K]^T on the matrix cores: the
-// 16-byte loads of A rows (lane l = row l % 16, elements 8 (l / 16) .. +7 of
-// a 32-wide step) and of packed B fragments are the MFMA operands as they
+// Two kernel templates compute C[M][N] = A[M][K] . B[N][K]^T on the matrix
+// cores.  For a few rows (decode sizes) the streaming kernel: the 16-byte
+// loads of A rows (lane l = row l % 16, elements 8 (l / 16) .. +7 of a
+// 32-wide step) and of packed B fragments are the MFMA operands as they
 // arrive, so nothing is staged through LDS.  A workgroup owns 16 output
 // columns and 16 * MT rows; its waves split the reduction and meet in LDS,
 // where wave 0 adds the parts and applies the epilogue.  For the gate/up
 // product the workgroup computes the gate and up tiles of the same columns
 // and writes silu(g) * u.  At decode sizes (M = a few tokens) the kernel
 // streams the weights once, each wave with all loads of its slice in flight.
+// For more rows the LDS-tiled kernel below.
 
 #include "device_common.h"
 #include "launch.h"
@@ -28,6 +30,7 @@
 namespace dqkv {
 
 typedef __bf16 aq_bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // W = waves splitting the reduction; STEPS = 32-wide reduction steps whose
 // loads are issued together (a wave's whole slice at decode sizes).
@@ -131,15 +134,215 @@ static hipError_t launch_gemm(const bf16* A, const bf16* B0, const bf16* B1, bf1
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ tiled product
+// Larger M: C[M][N] = A[M][K] . B[N][K]^T with both operands staged in LDS.
+// A workgroup (4 or 8 waves) owns BN weight rows x BM activation rows and
+// walks the reduction in 64-wide stages through S LDS buffers, every load
+// going from HBM straight into LDS (16-byte global_load_lds: lane l of a
+// wave instruction fills bytes 16 l .. 16 l + 15 of a 1 KiB block).
+//   * Weights: one instruction = one packed 1 KiB fragment (16 rows x 32
+//     reduction elements, contiguous in the packed weights); in LDS a
+//     16-lane group reads 256 contiguous bytes per operand.
+//   * Activations: one instruction = 8 rows x 128 bytes (full cache lines);
+//     LDS holds the rows row-major, logical 16-byte slot c of row r at
+//     physical slot c ^ ((r / 2) & 7) (the loads permute their sources), so
+//     the 16 rows an operand read serves at once meet 16 different 16-byte
+//     positions of the 64-bank LDS.
+// The matrix cores compute D = W_tile . A_tile^T, so lane l holds output
+// row m = l % 16 and four consecutive output columns 4 (l / 16) .. +3, stored
+// as 8 bytes.  For the gate/up product a wave's NF weight blocks are NF / 2
+// gate blocks followed by the up blocks of the same output columns, so
+// silu(g) * u pairs accumulators of the same lane and register.
+// s_waitcnt encoding (gfx9 family): vmcnt in bits 3:0 and 15:14, expcnt and
+// lgkmcnt left at their maxima (no wait).
+template <int N>
+struct VmWait {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  static constexpr int kImm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+};
+
+// BK = reduction elements per stage (64: one cache line per activation row),
+// S = LDS stages; the loads of stage k + S - 1 are issued while stage k is
+// multiplied.
+template <bool SWIGLU, int BN, int BM, int WN, int WM, int BK, int S>
+__global__ __launch_bounds__(64 * WN * WM) void augq_tiled_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ B0, const bf16* __restrict__ B1,
+    bf16* __restrict__ C, int M, int N, int K, int n_mtiles) {
+  constexpr int NW = WN * WM;               // waves per workgroup
+  static_assert((NW == 4 || NW == 8) && BK == 64 && S >= 2, "tile shape");
+  constexpr int KB = BK / 32;               // 32-wide blocks per stage
+  constexpr int NF = BN / WN / 16;          // weight blocks per wave
+  constexpr int MF = BM / WM / 16;          // activation blocks per wave
+  constexpr int BFR = BN / 16 * KB;         // weight fragments per stage
+  constexpr int AFR = BM / 16 * KB;         // activation fragments per stage
+  constexpr int FR = BFR + AFR;
+  constexpr int STAGE = FR * 1024;          // bytes
+  constexpr int LPW = FR / NW;              // fragment loads per wave per stage
+  static_assert(FR % NW == 0 && (!SWIGLU || NF % 2 == 0), "tile shape");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[S * STAGE];
+
+  // Consecutive logical tiles share a weight stripe; the renumbering puts
+  // them on one XCD (dispatch is round-robin over 8 XCDs) to share its L2.
+  const int nwg = gridDim.x, id = blockIdx.x;
+  const int logical = (nwg % 8 == 0) ? (id % 8) * (nwg / 8) + id / 8 : id;
+  const int mt = logical % n_mtiles, nt = logical / n_mtiles;
+  const int m0 = mt * BM;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave % WN, wm = wave / WN;
+  const int kb_n = K / 32;
+
+  // Sources of this wave's fragment loads (fragments wave, wave + NW, ...) at
+  // stage 0; a stage advances weights by KB fragments (512 elements each)
+  // and activations by BK elements.
+  const bf16* src[LPW];
+  bool is_w[LPW];
+#pragma unroll
+  for (int u = 0; u < LPW; ++u) {
+    const int f = wave + NW * u;
+    if (f < BFR) {
+      const int nbl = f / KB, kbl = f % KB;  // local 16-row weight block, k block
+      const bf16* Bsrc = B0;
+      int nb;
+      if constexpr (SWIGLU) {
+        const int g = nbl / NF, j = nbl % NF;   // wave-n group, block within it
+        Bsrc = j < NF / 2 ? B0 : B1;
+        nb = nt * (BN / 32) + g * (NF / 2) + j % (NF / 2);
+      } else {
+        nb = nt * (BN / 16) + nbl;
+      }
+      src[u] = Bsrc + ((size_t)nb * kb_n + kbl) * 512 + lane * 8;
+      is_w[u] = true;
+    } else {
+      // Activation load a: rows 8a .. 8a + 7 of the tile, 128 bytes each;
+      // lane l fills LDS slot l % 8 of row r = 8a + l / 8, which holds the
+      // row's logical 16-byte slot (l % 8) ^ ((r / 2) & 7).
+      const int a = f - BFR;
+      const int r = 8 * a + (lane >> 3);
+      const int row = min(m0 + r, M - 1);
+      src[u] = A + (size_t)row * K + 8 * ((lane & 7) ^ ((r >> 1) & 7));
+      is_w[u] = false;
+    }
+  }
+  auto issue = [&](int kt, int stage) {
+    unsigned char* dst = lds + stage * STAGE;
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const size_t adv = is_w[u] ? (size_t)kt * KB * 512 : (size_t)kt * BK;
+      // (The untyped source pointer also keeps the host pass emitting this
+      // kernel's launch stub.)
+      __builtin_amdgcn_global_load_lds((const void*)(src[u] + adv),
+                                       (lds_void_t*)(dst + (wave + NW * u) * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[NF][MF];
+#pragma unroll
+  for (int i = 0; i < NF; ++i)
+#pragma unroll
+    for (int j = 0; j < MF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / BK;
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k)
+    if (k < nk) issue(k, k);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt % S;
+    // Stage kt has landed for this wave (the loads of the S - 2 later stages
+    // may still be in flight; near the end wait for everything), then for
+    // every wave, and every wave is done with the stage that receives stage
+    // kt + S - 1.
+    if (kt + S - 2 < nk) __builtin_amdgcn_s_waitcnt(VmWait<(S - 2) * LPW>::kImm);
+    else __builtin_amdgcn_s_waitcnt(VmWait<0>::kImm);
+    __syncthreads();
+    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+    const unsigned char* base = lds + st * STAGE + lane * 16;
+#pragma unroll
+    for (int s = 0; s < KB; ++s) {
+      aq_bf16x8 wf[NF], af[MF];
+#pragma unroll
+      for (int i = 0; i < NF; ++i)
+        wf[i] = *reinterpret_cast<const aq_bf16x8*>(base + ((wn * NF + i) * KB + s) * 1024);
+#pragma unroll
+      for (int j = 0; j < MF; ++j) {
+        const int r = (wm * MF + j) * 16 + (lane & 15), c = 4 * s + (lane >> 4);
+        af[j] = *reinterpret_cast<const aq_bf16x8*>(lds + st * STAGE + BFR * 1024 + r * 128 +
+                                                   ((c ^ ((r >> 1) & 7)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < NF; ++i)
+#pragma unroll
+        for (int j = 0; j < MF; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // D[n][m]: lane l holds m = l % 16 and n = 4 (l / 16) .. +3 of its block.
+  const int l16 = lane & 15, q4 = 4 * (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < MF; ++j) {
+    const int m = m0 + (wm * MF + j) * 16 + l16;
+    if (m >= M) continue;
+    constexpr int NO = SWIGLU ? NF / 2 : NF;  // output blocks per wave
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (SWIGLU) {
+          const float g = acc[i][j][e];
+          v[e] = g / (1.f + fast_exp2(-g * kLog2e)) * acc[i + NF / 2][j][e];
+        } else {
+          v[e] = acc[i][j][e];
+        }
+      }
+      const int n = SWIGLU ? nt * (BN / 2) + (wn * NO + i) * 16 + q4
+                           : nt * BN + (wn * NF + i) * 16 + q4;
+      const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      *reinterpret_cast<uint2*>(C + (size_t)m * N + n) = make_uint2(w0, w1);
+    }
+  }
+}
+
+template <bool SWIGLU, int BN, int BM, int WN, int WM, int BK, int S>
+static hipError_t launch_tiled(const bf16* A, const bf16* B0, const bf16* B1, bf16* C, int M,
+                               int N, int K, hipStream_t stream) {
+  constexpr int OUT_N = SWIGLU ? BN / 2 : BN;  // output columns per tile
+  const int n_mtiles = (M + BM - 1) / BM;
+  const long long tiles = (long long)n_mtiles * (N / OUT_N);
+  hipLaunchKernelGGL((augq_tiled_kernel<SWIGLU, BN, BM, WN, WM, BK, S>), dim3((unsigned)tiles),
+                     dim3(64 * WN * WM), 0, stream, A, B0, B1, C, M, N, K, n_mtiles);
+  return hipGetLastError();
+}
+
 // Decode sizes (M <= 16): 16 rows per workgroup and sixteen waves on the
 // reduction, each issuing all loads of its slice (up to 8 steps) at once, so
-// the weights stream in about one memory round trip.  Larger M: 64 rows per
-// workgroup (each weight load feeds four products), eight waves, four steps
-// per round.
+// the weights stream in about one memory round trip.  Up to 64 rows: 64 rows
+// per workgroup (each weight load feeds four products), eight waves, four
+// steps per round.  Beyond that the LDS-tiled product: from 1024 rows eight
+// waves per workgroup on 192 x 256 gate/up tiles (96 output columns) and
+// 128 x 128 down tiles with three stages; below, four waves on 128 x 128
+// gate/up tiles (64 output columns) and 64 x 128 down tiles.  Widths that
+// do not divide into whole tiles take the 64-row kernel.
 template <bool SWIGLU>
 static hipError_t gemm(const bf16* A, const bf16* B0, const bf16* B1, bf16* C, int M, int N,
                        int K, hipStream_t stream) {
   if (M <= 16) return launch_gemm<1, SWIGLU, 16, 8>(A, B0, B1, C, M, N, K, stream);
+  if (M > 64 && K % 64 == 0) {
+    const bool big = M >= 1024;
+    if constexpr (SWIGLU) {
+      if (big && N % 96 == 0)
+        return launch_tiled<true, 192, 256, 2, 4, 64, 2>(A, B0, B1, C, M, N, K, stream);
+      if (N % 64 == 0)
+        return launch_tiled<true, 128, 128, 2, 2, 64, 2>(A, B0, B1, C, M, N, K, stream);
+    } else {
+      if (big && N % 128 == 0)
+        return launch_tiled<false, 128, 128, 2, 4, 64, 3>(A, B0, B1, C, M, N, K, stream);
+      if (N % 64 == 0)
+        return launch_tiled<false, 64, 128, 1, 4, 64, 2>(A, B0, B1, C, M, N, K, stream);
+    }
+  }
   return launch_gemm<4, SWIGLU, 8, 4>(A, B0, B1, C, M, N, K, stream);
 }
 

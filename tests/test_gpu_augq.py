@@ -36,7 +36,13 @@ SHAPES = [
     (5, 2048, 3072, 2048),     # SIGMA-1.5B, a few decode tokens
     (16, 1024, 2048, 512),
     (17, 1024, 1024, 64),      # first size that takes 64-row workgroups
-    (200, 2048, 3072, 2048),   # several 64-row tiles and a ragged tail
+    (64, 1024, 2048, 128),     # last size on the 64-row workgroups
+    (65, 1024, 1024, 64),      # first size on the LDS-tiled product, one ragged tile
+    (200, 2048, 3072, 2048),   # LDS-tiled: a full 128-row tile and a ragged tail
+    (300, 1024, 2048, 192),    # three row tiles, three 64-column down tiles
+    (130, 1024, 1024, 80),     # d_out not a multiple of 64: the down product stays untiled
+    (1100, 1024, 3072, 256),   # eight-wave tiles for both products, ragged last row tile
+    (1030, 1024, 1024, 128),   # d_i not a multiple of 96: four-wave gate/up, eight-wave down
 ]
 
 
@@ -85,3 +91,19 @@ def test_augq_rows_are_independent():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(q_all[[0, 17, 39]].view(torch.int16).cpu().numpy(),
                                   q_one.view(torch.int16).cpu().numpy())
+
+
+def test_augq_tiled_rows_do_not_depend_on_the_batch():
+    # On the LDS-tiled path a row's result depends on that row alone: the
+    # first 130 rows of a 260-row call equal a 130-row call bit for bit
+    # (same tile positions, different tile count and tail).
+    case = synth.make_augq(504, M=260, d_m=1024, d_i=2048, d_out=256)
+    h = to_dev(case.h, "bf16")
+    wg, wu, wd = (dq.augq_pack(to_dev(x, "bf16")) for x in (case.w_gate, case.w_up, case.w_down))
+    q_all = dq.augq(h, wg, wu, wd)
+    q_part = dq.augq(h[:130].contiguous(), wg, wu, wd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q_all[:130].view(torch.int16).cpu().numpy(),
+                                  q_part.view(torch.int16).cpu().numpy())
+    ref_q, _ = oracle.augq(*case.widened())
+    assert_close(to_host(q_all), ref_q, "bf16", "augq 260 rows")
