@@ -81,8 +81,14 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
 // lse); otherwise they add the bf16-rounded weights that the P.V product
 // multiplies, two per v_dot2_f32_bf16, which normalises O by exactly the
 // weights it used.
+// Waves per SIMD the register budget is cut for: three for d_k = 64,
+// d_v = 128 (167 VGPRs, no spills; the default allocation lands two
+// registers above the three-wave limit), the compiler's choice otherwise.
+template <int DK, int DV>
+constexpr int prefill_min_waves() { return (DK == 64 && DV == 128) ? 3 : 1; }
+
 template <int DK, int DV, bool kExactSum>
-__global__ __launch_bounds__(256) void prefill_kernel(
+__global__ __launch_bounds__(256, (prefill_min_waves<DK, DV>())) void prefill_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ ctx_len, bf16* __restrict__ out, float* __restrict__ lse,
     int n_q, int n_k, int n_v, int t_new, int l_cap, int n_qtiles, float qscale,
@@ -281,7 +287,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     __syncthreads();
     if (t + 1 < t_end) issue_tile(t + 1, sc ^ 1);
     const int j0 = t * kPfKeys;
+    // The matrix products run at raised wave priority, so the other wave on
+    // the SIMD fills the gaps with its softmax work.
+    __builtin_amdgcn_s_setprio(1);
     qk(stage_k(sc), sa);
+    __builtin_amdgcn_s_setprio(0);
     // Causal mask (only on tiles that reach past this wave's first row): key
     // j is visible to this row iff j <= p_q.
     if (j0 + kPfKeys - 1 > base + r0 + wave * kPfRowsPerWave) {
@@ -301,8 +311,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     // Software overlap inside the tile: the matrix products of keys 0-31 run
     // while the VALU computes P for keys 32-63.
     make_p(sa, 0, pb, psum, m_use);
+    __builtin_amdgcn_s_setprio(1);
     pv(stage_v(sc), 0, pb);
     pv(stage_v(sc), 1, pb);
+    __builtin_amdgcn_s_setprio(0);
     make_p(sa, 1, pb, psum, m_use);
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
@@ -312,8 +324,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     }
     psum += __shfl_xor(psum, 32);
     l_run += psum;
+    __builtin_amdgcn_s_setprio(1);
     pv(stage_v(sc), 2, pb);
     pv(stage_v(sc), 3, pb);
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // Store this lane's query row: rows 8*(r/4)+4h+r%4 of each 32-column block
