@@ -69,13 +69,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kPrefillRows = 128;  // query rows per prefill workgroup
 
-// Key splits for a prefill: enough workgroups for three per CU (so
-// matrix-core and softmax work of different waves overlap on each SIMD;
-// 48 KiB of LDS each), at most 4.
+// Key splits for a prefill: enough workgroups for two per CU (the kernel's
+// registers allow two waves per SIMD), at most 4.
 int plan_prefill_split(int n_q, int batch, int t_new) {
   const long long wg = (long long)batch * n_q * ((t_new + kPrefillRows - 1) / kPrefillRows);
   if (wg <= 0) return 1;
-  long long ns = (3LL * kCUs + wg - 1) / wg;  // three workgroups per CU
+  long long ns = (2LL * kCUs + wg - 1) / wg;
   if (ns < 1) ns = 1;
   if (ns > 4) ns = 4;
   return (int)ns;

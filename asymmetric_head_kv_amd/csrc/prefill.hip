@@ -8,7 +8,8 @@
 //
 // Work split: a workgroup = 4 waves = 128 consecutive query rows of one query
 // head; each wave owns 32 rows.  The workgroup walks the visible keys in
-// tiles of 64, double-buffered in LDS.  Tiles travel from HBM straight into
+// tiles of 64, double-buffered in LDS, software-pipelined so that the matrix
+// products of one tile overlap the softmax of another inside each wave.  Tiles travel from HBM straight into
 // LDS (16-byte global_load_lds, no register staging): K and V row-major, their
 // 16-byte slots XOR-swizzled by row against bank conflicts.  The V^T operand
 // is read with ds_read_b64_tr_b16, which hands each lane one value column for
@@ -81,14 +82,8 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
 // lse); otherwise they add the bf16-rounded weights that the P.V product
 // multiplies, two per v_dot2_f32_bf16, which normalises O by exactly the
 // weights it used.
-// Waves per SIMD the register budget is cut for: three for d_k = 64,
-// d_v = 128 (167 VGPRs, no spills; the default allocation lands two
-// registers above the three-wave limit), the compiler's choice otherwise.
-template <int DK, int DV>
-constexpr int prefill_min_waves() { return (DK == 64 && DV == 128) ? 3 : 1; }
-
 template <int DK, int DV, bool kExactSum>
-__global__ __launch_bounds__(256, (prefill_min_waves<DK, DV>())) void prefill_kernel(
+__global__ __launch_bounds__(256) void prefill_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ ctx_len, bf16* __restrict__ out, float* __restrict__ lse,
     int n_q, int n_k, int n_v, int t_new, int l_cap, int n_qtiles, float qscale,
@@ -165,10 +160,9 @@ __global__ __launch_bounds__(256, (prefill_min_waves<DK, DV>())) void prefill_ke
   }
   // Rows past n_keys (only in the last tile) are clamped to the last visible
   // row: the loads stay in bounds and every score they feed is masked.
-  auto issue_tile = [&](int t, int stage) {
+  auto issue_k = [&](int t, int stage) {
     const int j0 = t * kPfKeys;
     unsigned char* kl = lds + stage * Lds::kStage + wave_u * 1024;
-    unsigned char* vl = lds + stage * Lds::kStage + Lds::kKBytes + wave_u * 1024;
     const bool full = j0 + kPfKeys <= n_keys;
 #pragma unroll
     for (int r = 0; r < KR; ++r) {
@@ -176,6 +170,11 @@ __global__ __launch_bounds__(256, (prefill_min_waves<DK, DV>())) void prefill_ke
       __builtin_amdgcn_global_load_lds(kbase + (uint32_t)(j * DK + k_off[r]),
                                        (lds_void*)(kl + r * 4096), 16, 0, 0);
     }
+  };
+  auto issue_v = [&](int t, int stage) {
+    const int j0 = t * kPfKeys;
+    unsigned char* vl = lds + stage * Lds::kStage + Lds::kKBytes + wave_u * 1024;
+    const bool full = j0 + kPfKeys <= n_keys;
 #pragma unroll
     for (int r = 0; r < VR; ++r) {
       const int j = full ? j0 + v_row[r] : min(j0 + v_row[r], n_keys - 1);
@@ -222,11 +221,9 @@ __global__ __launch_bounds__(256, (prefill_min_waves<DK, DV>())) void prefill_ke
       }
     }
   };
-  // Running max from a tile's scores.  Lazy rescaling: the running max only
-  // moves (and O, l are rescaled) when some row's max grows by more than
-  // 2^8; otherwise the stale max is kept, probabilities stay <= 256, and
-  // O / l is unchanged.
-  auto prep = [&](const f32x16 (&sx)[2]) {
+  // A tile's row maximum of the scaled scores (the two lane halves of a
+  // query row joined by one shuffle).
+  auto tile_max = [&](const f32x16 (&sx)[2]) -> float {
     float smax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -234,7 +231,12 @@ __global__ __launch_bounds__(256, (prefill_min_waves<DK, DV>())) void prefill_ke
       for (int r = 0; r < 16; r += 2) smax = fmaxf(fmaxf(smax, sx[kb][r]), sx[kb][r + 1]);
     }
     smax = fmaxf(smax, __shfl_xor(smax, 32));
-    const float m_tile = smax * qscale;
+    return smax * qscale;
+  };
+  // Lazy rescaling: the running max only moves (and O, l are rescaled) when
+  // some row's max grows by more than 2^8; otherwise the stale max is kept,
+  // probabilities stay <= 256, and O / l is unchanged.
+  auto rescale = [&](float m_tile) {
     if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.f) != 0) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
@@ -242,6 +244,21 @@ __global__ __launch_bounds__(256, (prefill_min_waves<DK, DV>())) void prefill_ke
 #pragma unroll
       for (int n = 0; n < NB; ++n) o[n] *= alpha;
       m_run = m_new;
+    }
+  };
+  // Causal mask of tile t (only tiles that reach past this wave's first
+  // row): key j is visible to this row iff j <= p_q.
+  auto mask = [&](f32x16 (&sx)[2], int t) {
+    const int j0 = t * kPfKeys;
+    if (j0 + kPfKeys - 1 > base + r0 + wave * kPfRowsPerWave) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + kb * 32 + (r >> 2) * 8 + 4 * h + (r & 3);
+          sx[kb][r] = j <= p_q ? sx[kb][r] : -INFINITY;
+        }
+      }
     }
   };
   // P for one 32-key block: exponentials, row sums, bf16 operands.
@@ -276,59 +293,80 @@ __global__ __launch_bounds__(256, (prefill_min_waves<DK, DV>())) void prefill_ke
     return lds + st * Lds::kStage + Lds::kKBytes;
   };
 
-  // Two LDS stages: tile t is consumed while tile t + 1 arrives.
-  if (t_begin < t_end) issue_tile(t_begin, 0);
-  f32x16 sa[2];
-  for (int t = t_begin; t < t_end; ++t) {
-    const int sc = (t - t_begin) & 1;
-    // Tile t has landed for every wave, and every wave is done with tile
-    // t - 1, whose stage now receives tile t + 1.
+  // Software pipeline over key tiles, K one tile ahead of V: iteration t
+  // finds K(t + 1) and V(t) in LDS and S^T(t) in registers, requests K(t + 2)
+  // and V(t + 1), and runs three phases that each pair matrix-core work with
+  // independent VALU work of the same wave:
+  //   A: S^T(t + 1) = K(t + 1) Q^T      with  P(t) for keys 0-31
+  //   B: O^T += V^T(t) P^T, keys 0-31   with  P(t) for keys 32-63
+  //   C: O^T += V^T(t) P^T, keys 32-63  with  the row max of S^T(t + 1)
+  // LDS stage s holds K of tiles t_begin + s, + s + 2, ... and V of the same
+  // tiles, each loaded one iteration apart.  (On the last iteration phase A
+  // multiplies a stale K stage; its result is never used.)
+  f32x16 sa0[2], sa1[2];
+  float m_tile = -INFINITY;
+  if (t_begin < t_end) {
+    issue_k(t_begin, 0);
+    issue_v(t_begin, 0);
+    if (t_begin + 1 < t_end) issue_k(t_begin + 1, 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < t_end) issue_tile(t + 1, sc ^ 1);
-    const int j0 = t * kPfKeys;
-    // The matrix products run at raised wave priority, so the other wave on
-    // the SIMD fills the gaps with its softmax work.
-    __builtin_amdgcn_s_setprio(1);
-    qk(stage_k(sc), sa);
-    __builtin_amdgcn_s_setprio(0);
-    // Causal mask (only on tiles that reach past this wave's first row): key
-    // j is visible to this row iff j <= p_q.
-    if (j0 + kPfKeys - 1 > base + r0 + wave * kPfRowsPerWave) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + kb * 32 + (r >> 2) * 8 + 4 * h + (r & 3);
-          sa[kb][r] = j <= p_q ? sa[kb][r] : -INFINITY;
-        }
-      }
-    }
-    prep(sa);
+    qk(stage_k(0), sa0);
+    mask(sa0, t_begin);
+    m_tile = tile_max(sa0);
+  }
+  auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], int t) {
+    const int i = t - t_begin;
+    const int cur = i & 1, nxt = cur ^ 1;
+    // K(t + 1) and V(t) have landed for every wave; every wave is done with
+    // K(t) and V(t - 1), whose places receive K(t + 2) and V(t + 1).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 2 < t_end) issue_k(t + 2, cur);
+    if (t + 1 < t_end) issue_v(t + 1, nxt);
+    rescale(m_tile);
     const float m_use = m_run == -INFINITY ? 0.f : m_run;  // rows with nothing visible yet
     float psum = 0.f;
     bf16x8 pb[4];
-    // Software overlap inside the tile: the matrix products of keys 0-31 run
-    // while the VALU computes P for keys 32-63.
-    make_p(sa, 0, pb, psum, m_use);
-    __builtin_amdgcn_s_setprio(1);
-    pv(stage_v(sc), 0, pb);
-    pv(stage_v(sc), 1, pb);
-    __builtin_amdgcn_s_setprio(0);
-    make_p(sa, 1, pb, psum, m_use);
+    qk(stage_k(nxt), sn);
+    make_p(sc, 0, pb, psum, m_use);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int k = 0; k < 2 * NB; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+    for (int k = 0; k < 2 * KS; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read for a later MFMA
+    }
+    pv(stage_v(cur), 0, pb);
+    pv(stage_v(cur), 1, pb);
+    make_p(sc, 1, pb, psum, m_use);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int k = 0; k < 2 * NB; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads for a later MFMA
     }
     psum += __shfl_xor(psum, 32);
     l_run += psum;
-    __builtin_amdgcn_s_setprio(1);
-    pv(stage_v(sc), 2, pb);
-    pv(stage_v(sc), 3, pb);
-    __builtin_amdgcn_s_setprio(0);
+    mask(sn, t + 1);
+    pv(stage_v(cur), 2, pb);
+    pv(stage_v(cur), 3, pb);
+    m_tile = tile_max(sn);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int k = 0; k < 2 * NB; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads for a later MFMA
+    }
+  };
+  int t = t_begin;
+  for (; t + 1 < t_end; t += 2) {
+    step(sa0, sa1, t);
+    step(sa1, sa0, t + 1);
   }
+  if (t < t_end) step(sa0, sa1, t);
 
   // Store this lane's query row: rows 8*(r/4)+4h+r%4 of each 32-column block
   // of O^T are value columns.  One split: normalise and write bf16 out / lse.

@@ -149,11 +149,11 @@ def test_prefill_validation(lib):
 
 
 def test_prefill_workspace_plan(lib):
-    # 2048 rows x 16 heads = 256 workgroups of 128 rows: three key splits so
-    # that every CU gets three workgroups; large launches run unsplit.
+    # 2048 rows x 16 heads = 256 workgroups of 128 rows: two key splits so
+    # that every CU gets two workgroups; large launches run unsplit.
     need = dq.prefill_workspace_bytes(16, 4, 16, 64, 128, 1, 2048)
     rows = 2048 * 16
-    assert need == -(-3 * rows * 128 * 4 // 256) * 256 + 3 * rows * 4
+    assert need == -(-2 * rows * 128 * 4 // 256) * 256 + 2 * rows * 4
     assert dq.prefill_workspace_bytes(16, 4, 16, 64, 128, 8, 4096) == 0
 
 
