@@ -13,7 +13,16 @@ namespace {
 
 constexpr int kCUs = 256;             // MI355X compute units
 constexpr int kWavesPerCUTarget = 8;  // split waves to aim for per CU
-constexpr int kMaxChunks = 8192;      // combine keeps one weight per chunk in LDS
+constexpr int kMaxChunks = 8192;      // bounds the workspace and the combine's loop
+// Batches of at least kRaggedBatch sequences plan kRaggedOversub times more
+// split workgroups: the host cannot see the lengths (they stay on the
+// device), and when they differ the chunks past a short sequence's end are
+// empty, so with one planned round many CU slots would sit idle.  With more,
+// smaller chunks the dispatcher refills them (16 sequences of 4k..32k rows:
+// 276 -> 253 us; uniform 4 x 64k loses 3% at that chunk length, so small
+// batches keep one round).
+constexpr int kRaggedBatch = 8;
+constexpr int kRaggedOversub = 8;
 constexpr int kMinChunk = 64;
 
 bool is_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
@@ -36,12 +45,13 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int to_status(hipError_t e) { return e == hipSuccess ? DQKV_OK : DQKV_ERR_HIP; }
 
 // Rows per context chunk: enough (sequence, head-quad, chunk) workgroups to
-// give every CU about kWavesPerCUTarget waves, in multiples of 64 rows.
-// H = query heads per wave.
+// give every CU about kWavesPerCUTarget waves (times kRaggedOversub for
+// large batches), in multiples of 64 rows.  H = query heads per wave.
 int plan_chunk_h(int n_q, int H, int batch, int max_ctx) {
   long long quads = (long long)batch * ((n_q / H + 3) / 4);
   if (quads < 1) quads = 1;  // an empty batch launches nothing
-  const long long want_wg = (long long)kCUs * kWavesPerCUTarget / 4;
+  const long long want_wg = (long long)kCUs * kWavesPerCUTarget / 4 *
+                            (batch >= kRaggedBatch ? kRaggedOversub : 1);
   long long chunks_per_seq = (want_wg + quads - 1) / quads;
   if (chunks_per_seq < 1) chunks_per_seq = 1;
   long long S = (max_ctx + chunks_per_seq - 1) / chunks_per_seq;

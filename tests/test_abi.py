@@ -108,6 +108,11 @@ def test_workspace_and_chunk_plan(lib):
     # Long single sequence: enough chunks to spread over the chip.
     S = dq.decode_chunk(16, 4, 16, 64, 128, 1, 32768)
     assert 32768 // S >= 64
+    # Large batches (lengths unknown to the host, possibly ragged) plan about
+    # eight times more chunks than a small batch of the same capacity would.
+    S4 = dq.decode_chunk(16, 4, 16, 64, 128, 4, 65536)
+    S16 = dq.decode_chunk(16, 4, 16, 64, 128, 16, 32769)
+    assert 65536 // S4 == 32 and -(-32769 // S16) >= 32
     # Explicit chunk lengths are honoured.
     assert dq.decode_workspace_bytes(16, 4, 16, 64, 128, 1, 4096, 64) == \
         -(-16 * 64 * 8 // 256) * 256 + 16 * 64 * 128 * 4
