@@ -8,10 +8,11 @@
 //
 // Work split: a workgroup = 4 waves = 128 consecutive query rows of one query
 // head; each wave owns 32 rows.  The workgroup walks the visible keys in
-// tiles of 64, double-buffered in LDS, software-pipelined so that the matrix
-// products of one tile overlap the softmax of another inside each wave.  Tiles travel from HBM straight into
-// LDS (16-byte global_load_lds, no register staging): K and V row-major, their
-// 16-byte slots XOR-swizzled by row against bank conflicts.  The V^T operand
+// tiles of 64 through two LDS stages, software-pipelined so that the matrix
+// products of one tile overlap the softmax of another inside each wave (see
+// the key loop).  Tiles travel from HBM straight into LDS (16-byte
+// global_load_lds, no register staging): K and V row-major, their 16-byte
+// slots XOR-swizzled by row against bank conflicts.  The V^T operand
 // is read with ds_read_b64_tr_b16, which hands each lane one value column for
 // four consecutive keys, so V needs no rearranging.  Everything is computed
 // transposed so that each lane owns one query row:
