@@ -70,6 +70,8 @@ def parse():
     p.add_argument("--ket", action="store_true",
                    help="only run the kernel-execution-time comparison of the pages' SIGMA-1.5B "
                         "and standard GQA attention shapes at prefixes 2k-32k and exit")
+    p.add_argument("--only-augq", action="store_true",
+                   help="only run the augmented-Q leg (1, 16 and 2048 tokens) and exit")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES bytes three times (calibrates "
                         "the HBM byte counters of a profiler) and exit")
@@ -605,7 +607,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
-              "is not sharded across GPUs in this build.", file=sys.stderr)
+              "is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -620,6 +622,9 @@ def main():
         print(json.dumps({"copy_probe_bytes": a.numel() * 4, "copies": 3}))
         return
 
+    if args.only_augq:
+        print(json.dumps({"augq": augq_bench(args.steps)}), flush=True)
+        return
     if args.ket:
         print(json.dumps({"ket_replica": ket_replica(args.steps),
                           "note": "batch 1, one query token, bf16; kernel times from graphs "
