@@ -135,3 +135,26 @@ def test_paged_random_shapes(seed):
     ref, _ = oracle.decode(qw, kw, vw, case.ctx_len, case.scale)
     err = assert_close(to_host(out), ref, dtype, f"seed {seed}")
     _say(f"  normwise rel err {err:.2e}")
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_decode_large_ragged_batch(seed):
+    # Batches of eight or more sequences plan smaller chunks (the lengths are
+    # not known on the host): many chunks are empty for the short sequences.
+    rng = np.random.default_rng(4000 + seed)
+    B = int(rng.integers(8, 17))
+    lens = [int(x) for x in rng.integers(1, 3000, size=B)]
+    lens[int(rng.integers(B))] = 3000
+    dtype = ["bf16", "f32"][seed % 2]
+    _say("large ragged batch", seed, dtype, B, lens)
+    case = synth.make_case(950 + seed, dtype=dtype, batch=B, n_q=16, n_k=4, n_v=16, d_k=64,
+                           d_v=128, ctx_len=lens, l_cap=3000, poison_tail=True)
+    q, k, v, ctx = upload(case)
+    lse = torch.empty((B, 16), dtype=torch.float32, device="cuda")
+    out, _ = dq.decode(q, k, v, ctx, scale=case.scale, lse=lse)
+    torch.cuda.synchronize()
+    qw, kw, vw = case.widened()
+    ref, ref_lse = oracle.decode(qw, kw, vw, case.ctx_len, case.scale)
+    err = assert_close(to_host(out), ref, dtype, f"seed {seed}")
+    assert_lse_close(to_host(lse), ref_lse, dtype, f"seed {seed}")
+    _say(f"  normwise rel err {err:.2e}")
