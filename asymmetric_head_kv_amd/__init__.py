@@ -103,9 +103,21 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+def _stream(stream, dev) -> int:
+    """The HIP stream to launch on: the tensors' device's current stream, or
+    the given one (which must belong to that device)."""
+    if stream is None:
+        return torch.cuda.current_stream(dev).cuda_stream
+    if stream.device != dev:
+        raise ValueError("stream is on another device than the tensors")
+    return stream.cuda_stream
+
+
+def _call(dev, fn: str, *args) -> None:
+    """Call a library entry point with the tensors' device current, so its
+    kernels launch on the GPU that holds the data."""
+    with torch.cuda.device(dev):
+        _check(fn, getattr(load(), fn)(*args))
 
 
 def _device_tensors(*ts):
@@ -144,7 +156,7 @@ def decode_workspace_bytes(n_q, n_k, n_v, d_k, d_v, batch, max_ctx,
 
 def kv_append(k_new, v_new, pos, k_cache, v_cache, *, n_q=None, stream=None):
     """Write token-major rows k_new/v_new into the caches at rows pos[b] + t."""
-    _device_tensors(k_new, v_new, pos, k_cache, v_cache)
+    dev = _device_tensors(k_new, v_new, pos, k_cache, v_cache)
     B, T, n_k, d_k = k_new.shape
     n_v, d_v = v_new.shape[2], v_new.shape[3]
     if k_cache.shape[:2] != (B, n_k) or v_cache.shape[:2] != (B, n_v) or \
@@ -157,9 +169,9 @@ def kv_append(k_new, v_new, pos, k_cache, v_cache, *, n_q=None, stream=None):
         if t.dtype != k_new.dtype:
             raise TypeError("k_new, v_new and the caches must share one dtype")
     n_q = max(n_k, n_v) if n_q is None else n_q
-    _check("kv_append", load().kv_append(
-        n_q, n_k, n_v, d_k, d_v, _dtype_code(k_new), B, T, k_cache.shape[2],
-        _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(k_cache), _ptr(v_cache), _stream(stream)))
+    _call(dev, "kv_append",
+          n_q, n_k, n_v, d_k, d_v, _dtype_code(k_new), B, T, k_cache.shape[2],
+          _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(k_cache), _ptr(v_cache), _stream(stream, dev))
 
 
 def decode(q, k_cache, v_cache, ctx_len, *, max_ctx=None, scale=None, out=None,
@@ -169,7 +181,7 @@ def decode(q, k_cache, v_cache, ctx_len, *, max_ctx=None, scale=None, out=None,
 
     With k_new [B, n_k, d_k] / v_new [B, n_v, d_v] the step first appends
     them at cache row ctx_len[b] - 1 (diffqkv_decode_append)."""
-    _device_tensors(q, k_cache, v_cache, ctx_len, out, lse, workspace, k_new, v_new)
+    dev = _device_tensors(q, k_cache, v_cache, ctx_len, out, lse, workspace, k_new, v_new)
     B, n_q, d_k = q.shape
     n_k, l_cap = k_cache.shape[1], k_cache.shape[2]
     n_v, d_v = v_cache.shape[1], v_cache.shape[3]
@@ -197,16 +209,16 @@ def decode(q, k_cache, v_cache, ctx_len, *, max_ctx=None, scale=None, out=None,
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     if k_new is None:
-        _check("diffqkv_decode", load().diffqkv_decode(
-            n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, l_cap, max_ctx, scale,
-            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(out), _ptr(lse),
-            int(chunk_tokens), _ptr(workspace), ws_bytes, _stream(stream)))
+        _call(dev, "diffqkv_decode",
+              n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, l_cap, max_ctx, scale,
+              _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(out), _ptr(lse),
+              int(chunk_tokens), _ptr(workspace), ws_bytes, _stream(stream, dev))
     else:
-        _check("diffqkv_decode_append", load().diffqkv_decode_append(
-            n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, l_cap, max_ctx, scale,
-            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
-            _ptr(out), _ptr(lse), int(chunk_tokens), _ptr(workspace), ws_bytes,
-            _stream(stream)))
+        _call(dev, "diffqkv_decode_append",
+              n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, l_cap, max_ctx, scale,
+              _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
+              _ptr(out), _ptr(lse), int(chunk_tokens), _ptr(workspace), ws_bytes,
+              _stream(stream, dev))
     return out, lse
 
 
@@ -226,7 +238,8 @@ def decode_selective(q, k_cache, v_cache, ctx_len, *, top_k=100, max_ctx=None, s
     softmax) weights.  Returns (out [B, n_q, d_v], lse or None, sel_idx or
     None); pass sel_idx (int32 [B, n_q, top_k]) to receive the chosen rows.
     k_new / v_new fuse the append of the step's token as in decode()."""
-    _device_tensors(q, k_cache, v_cache, ctx_len, out, lse, sel_idx, workspace, k_new, v_new)
+    dev = _device_tensors(q, k_cache, v_cache, ctx_len, out, lse, sel_idx, workspace, k_new,
+                          v_new)
     B, n_q, d_k = q.shape
     n_k, l_cap = k_cache.shape[1], k_cache.shape[2]
     n_v, d_v = v_cache.shape[1], v_cache.shape[3]
@@ -255,11 +268,11 @@ def decode_selective(q, k_cache, v_cache, ctx_len, *, top_k=100, max_ctx=None, s
     if workspace is None:
         need = selective_workspace_bytes(n_q, n_k, n_v, d_k, d_v, B, max_ctx, top_k)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _check("diffqkv_decode_selective", load().diffqkv_decode_selective(
-        n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, l_cap, max_ctx, scale, top_k,
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
-        _ptr(out), _ptr(lse), _ptr(sel_idx), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+    _call(dev, "diffqkv_decode_selective",
+          n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, l_cap, max_ctx, scale, top_k,
+          _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
+          _ptr(out), _ptr(lse), _ptr(sel_idx), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(stream, dev))
     return out, lse, sel_idx
 
 
@@ -277,7 +290,7 @@ def kv_append_paged(k_new, v_new, pos, block_table, k_pages, v_pages, *, n_q=Non
                     stream=None):
     """kv_append into a paged cache: token t of sequence b goes to row
     pos[b] + t, i.e. slot (row % P) of page block_table[b, row // P]."""
-    _device_tensors(k_new, v_new, pos, block_table, k_pages, v_pages)
+    dev = _device_tensors(k_new, v_new, pos, block_table, k_pages, v_pages)
     B, T, n_k, d_k = k_new.shape
     num_pages, n_k2, P, d_k2, n_v, d_v, max_blocks = _pages_shape(k_pages, v_pages,
                                                                   block_table, B)
@@ -285,11 +298,14 @@ def kv_append_paged(k_new, v_new, pos, block_table, k_pages, v_pages, *, n_q=Non
         raise ValueError("inconsistent page / new-row shapes")
     if pos.dtype != torch.int32 or pos.numel() != B:
         raise ValueError("pos must be int32 [B]")
+    for t in (v_new, k_pages, v_pages):
+        if t.dtype != k_new.dtype:
+            raise TypeError("k_new, v_new and the page pools must share one dtype")
     n_q = max(n_k, n_v) if n_q is None else n_q
-    _check("kv_append_paged", load().kv_append_paged(
-        n_q, n_k, n_v, d_k, d_v, _dtype_code(k_new), B, T, P, num_pages, max_blocks,
-        _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(block_table), _ptr(k_pages), _ptr(v_pages),
-        _stream(stream)))
+    _call(dev, "kv_append_paged",
+          n_q, n_k, n_v, d_k, d_v, _dtype_code(k_new), B, T, P, num_pages, max_blocks,
+          _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(block_table), _ptr(k_pages), _ptr(v_pages),
+          _stream(stream, dev))
 
 
 def decode_paged(q, k_pages, v_pages, block_table, ctx_len, *, max_ctx=None, scale=None,
@@ -297,8 +313,8 @@ def decode_paged(q, k_pages, v_pages, block_table, ctx_len, *, max_ctx=None, sca
                  stream=None):
     """decode() over a paged cache (k_pages [N, n_k, P, d_k], v_pages
     [N, n_v, P, d_v], block_table int32 [B, max_blocks])."""
-    _device_tensors(q, k_pages, v_pages, block_table, ctx_len, out, lse, workspace, k_new,
-                    v_new)
+    dev = _device_tensors(q, k_pages, v_pages, block_table, ctx_len, out, lse, workspace, k_new,
+                          v_new)
     B, n_q, d_k = q.shape
     num_pages, n_k, P, d_k2, n_v, d_v, max_blocks = _pages_shape(k_pages, v_pages,
                                                                  block_table, B)
@@ -306,27 +322,36 @@ def decode_paged(q, k_pages, v_pages, block_table, ctx_len, *, max_ctx=None, sca
         raise ValueError("q and k_pages disagree on d_k")
     if ctx_len.dtype != torch.int32 or ctx_len.numel() != B:
         raise ValueError("ctx_len must be int32 [B]")
+    for t in (k_pages, v_pages, k_new, v_new):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError("q, the page pools and the new rows must share one dtype")
     if (k_new is None) != (v_new is None):
         raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None and (k_new.numel() != B * n_k * d_k or v_new.numel() != B * n_v * d_v):
+        raise ValueError("k_new must hold [B, n_k, d_k] and v_new [B, n_v, d_v]")
     max_ctx = max_blocks * P if max_ctx is None else int(max_ctx)
     scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
     if out is None:
         out = torch.empty((B, n_q, d_v), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, n_q, d_v) or out.dtype != q.dtype:
+        raise ValueError("out must be [B, n_q, d_v] in q's dtype")
+    if lse is not None and (lse.shape != (B, n_q) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, n_q]")
     need = decode_workspace_bytes(n_q, n_k, n_v, d_k, d_v, B, max_ctx, chunk_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _check("diffqkv_decode_paged", load().diffqkv_decode_paged(
-        n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, P, num_pages, max_blocks, max_ctx, scale,
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
-        _ptr(ctx_len), _ptr(out), _ptr(lse), int(chunk_tokens), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+    _call(dev, "diffqkv_decode_paged",
+          n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, P, num_pages, max_blocks, max_ctx, scale,
+          _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+          _ptr(ctx_len), _ptr(out), _ptr(lse), int(chunk_tokens), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(stream, dev))
     return out, lse
 
 
 def kv_group_sharing(k_cache, v_cache, *, n_q=None, stream=None):
     """Expand the side with fewer heads to max(n_k, n_v) heads (each head
     repeated in place); returns new (k, v) tensors."""
-    _device_tensors(k_cache, v_cache)
+    dev = _device_tensors(k_cache, v_cache)
     B, n_k, l_cap, d_k = k_cache.shape
     n_v, d_v = v_cache.shape[1], v_cache.shape[3]
     if v_cache.shape[0] != B or v_cache.shape[2] != l_cap or v_cache.dtype != k_cache.dtype:
@@ -335,21 +360,22 @@ def kv_group_sharing(k_cache, v_cache, *, n_q=None, stream=None):
     n_q = n_h if n_q is None else n_q
     k_out = torch.empty((B, n_h, l_cap, d_k), dtype=k_cache.dtype, device=k_cache.device)
     v_out = torch.empty((B, n_h, l_cap, d_v), dtype=v_cache.dtype, device=v_cache.device)
-    _check("kv_group_sharing", load().kv_group_sharing(
-        n_q, n_k, n_v, d_k, d_v, _dtype_code(k_cache), B, l_cap, _ptr(k_cache), _ptr(v_cache),
-        _ptr(k_out), _ptr(v_out), _stream(stream)))
+    _call(dev, "kv_group_sharing",
+          n_q, n_k, n_v, d_k, d_v, _dtype_code(k_cache), B, l_cap, _ptr(k_cache), _ptr(v_cache),
+          _ptr(k_out), _ptr(v_out), _stream(stream, dev))
     return k_out, v_out
 
 
 def augq_pack(w, *, stream=None):
     """Pack a bf16 weight [n_out, n_in] (out, in layout) for augq: returns
     [n_out // 16, n_in // 32, 64, 8] in matrix-core fragment order."""
-    _device_tensors(w)
+    dev = _device_tensors(w)
     if w.dtype != torch.bfloat16 or w.dim() != 2:
         raise TypeError("augq_pack takes a 2-D bfloat16 weight")
     n_out, n_in = w.shape
     wp = torch.empty((n_out // 16, n_in // 32, 64, 8), dtype=torch.bfloat16, device=w.device)
-    _check("augq_pack", load().augq_pack(n_out, n_in, _ptr(w), _ptr(wp), _stream(stream)))
+    _call(dev, "augq_pack",
+          n_out, n_in, _ptr(w), _ptr(wp), _stream(stream, dev))
     return wp
 
 
@@ -357,7 +383,7 @@ def augq(h, w_gate_p, w_up_p, w_down_p, *, out=None, workspace=None, stream=None
     """Augmented-Q projection, bf16: q = (silu(h W_gate^T) * h W_up^T) W_down^T.
     h [M, d_m]; weights packed by augq_pack (w_gate, w_up from [d_i, d_m],
     w_down from [d_out, d_i]).  Returns q [M, d_out]."""
-    _device_tensors(h, w_gate_p, w_up_p, w_down_p, out, workspace)
+    dev = _device_tensors(h, w_gate_p, w_up_p, w_down_p, out, workspace)
     M, d_m = h.shape
     d_i = w_gate_p.shape[0] * 16
     d_out = w_down_p.shape[0] * 16
@@ -369,13 +395,15 @@ def augq(h, w_gate_p, w_up_p, w_down_p, *, out=None, workspace=None, stream=None
             raise TypeError("augq takes bfloat16 tensors")
     if out is None:
         out = torch.empty((M, d_out), dtype=torch.bfloat16, device=h.device)
+    elif out.shape != (M, d_out) or out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16 [M, d_out]")
     need = _sz()
     _check("augq_workspace", load().augq_workspace(M, d_m, d_i, d_out, ctypes.byref(need)))
     if workspace is None:
         workspace = torch.empty(max(need.value, 16), dtype=torch.uint8, device=h.device)
-    _check("augq_forward", load().augq_forward(
-        M, d_m, d_i, d_out, _ptr(h), _ptr(w_gate_p), _ptr(w_up_p), _ptr(w_down_p), _ptr(out),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    _call(dev, "augq_forward",
+          M, d_m, d_i, d_out, _ptr(h), _ptr(w_gate_p), _ptr(w_up_p), _ptr(w_down_p), _ptr(out),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
     return out
 
 
@@ -393,7 +421,7 @@ def prefill(q, k_cache, v_cache, ctx_len, *, scale=None, out=None, lse=None,
 
     A workspace of prefill_workspace_bytes is allocated when none is given
     (pass one to avoid the allocation; an empty tensor runs unsplit)."""
-    _device_tensors(q, k_cache, v_cache, ctx_len, out, lse, workspace)
+    dev = _device_tensors(q, k_cache, v_cache, ctx_len, out, lse, workspace)
     B, T, n_q, d_k = q.shape
     n_k, l_cap = k_cache.shape[1], k_cache.shape[2]
     n_v, d_v = v_cache.shape[1], v_cache.shape[3]
@@ -401,6 +429,8 @@ def prefill(q, k_cache, v_cache, ctx_len, *, scale=None, out=None, lse=None,
         raise ValueError("inconsistent q / cache shapes")
     if ctx_len.dtype != torch.int32 or ctx_len.numel() != B:
         raise ValueError("ctx_len must be int32 [B]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
     scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
     if out is None:
         out = torch.empty((B, T, n_q, d_v), dtype=q.dtype, device=q.device)
@@ -411,8 +441,8 @@ def prefill(q, k_cache, v_cache, ctx_len, *, scale=None, out=None, lse=None,
     if workspace is None:
         need = prefill_workspace_bytes(n_q, n_k, n_v, d_k, d_v, B, T)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _check("diffqkv_prefill", load().diffqkv_prefill(
-        n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, T, l_cap, scale,
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(out), _ptr(lse),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    _call(dev, "diffqkv_prefill",
+          n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, T, l_cap, scale,
+          _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(out), _ptr(lse),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
     return out, lse

@@ -202,3 +202,26 @@ def test_paged_full_workload(P):
     err = assert_close(to_host(out_p), ref, "bf16", "paged 32k")
     assert_lse_close(to_host(lse_p), ref_lse, "bf16", "paged 32k")
     _say(f"  normwise rel err {err:.2e}")
+
+
+def test_binding_rejects_mismatched_paged_arguments():
+    # The binding checks dtypes and shapes before anything is launched: one
+    # dtype code travels over the C ABI, so a mismatch would be misread.
+    q = torch.zeros((1, 4, 64), dtype=torch.float32, device="cuda")
+    kp = torch.zeros((2, 1, 64, 64), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros((2, 4, 64, 64), dtype=torch.bfloat16, device="cuda")
+    table = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    ctx = torch.full((1,), 64, dtype=torch.int32, device="cuda")
+    with pytest.raises(TypeError):
+        dq.decode_paged(q, kp, vp, table, ctx)
+    qb = q.to(torch.bfloat16)
+    with pytest.raises(ValueError):
+        dq.decode_paged(qb, kp, vp, table, ctx, out=torch.empty((1, 4, 32), dtype=torch.bfloat16,
+                                                                 device="cuda"))
+    with pytest.raises(ValueError):
+        dq.decode_paged(qb, kp, vp, table, ctx, lse=torch.empty((1, 4), dtype=torch.bfloat16,
+                                                                 device="cuda"))
+    kn = torch.zeros((1, 1, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(TypeError):
+        dq.kv_append_paged(kn.view(1, 1, 1, 64), kn.new_zeros((1, 1, 4, 64)),
+                           ctx, table, kp, vp)
