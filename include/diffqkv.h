@@ -141,10 +141,11 @@ int32_t diffqkv_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
  * ctx_len counts rows after the append, Step 2 of section 3.4), and every
  * query head then attends rows 0 .. ctx_len[b] - 1 as in diffqkv_decode.
  * Same result, bit for bit, as kv_append with pos[b] = ctx_len[b] - 1
- * followed by diffqkv_decode, in two kernels instead of three: the split
- * kernel that owns row ctx_len[b] - 1 reads the new row from k_new / v_new
- * and stores it.  Requires 1 <= ctx_len[b] <= max_ctx for every b that
- * should append (ctx_len[b] = 0: nothing appended, out = 0, lse = -inf).
+ * followed by diffqkv_decode, in two kernels instead of three: the waves of
+ * the split workgroup that owns row ctx_len[b] - 1 store the new row into
+ * the caches and read it back with the rest of their chunk.  Requires
+ * 1 <= ctx_len[b] <= max_ctx for every b that should append (ctx_len[b] = 0:
+ * nothing appended, out = 0, lse = -inf).
  */
 int32_t diffqkv_decode_append(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
                               int32_t d_v, int32_t dtype, int32_t batch,
