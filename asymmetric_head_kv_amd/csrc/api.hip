@@ -572,7 +572,7 @@ int32_t augq_forward(int32_t M, int32_t d_m, int32_t d_i, int32_t d_out, const v
   if (M == 0) return DQKV_OK;
   if (!h || !w_gate || !w_up || !w_down || !q || !workspace) return DQKV_ERR_NULL;
   if (!aligned16(h) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
-      !aligned16(workspace))
+      !aligned16(q) || !aligned16(workspace))
     return DQKV_ERR_ALIGN;
   if (workspace_bytes_given < (size_t)M * d_i * 2) return DQKV_ERR_WORKSPACE;
   dqkv::AugQArgs a;

@@ -331,9 +331,9 @@ int32_t kv_group_sharing(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
  * in) layout: w_gate, w_up from [d_i][d_m], w_down from [d_out][d_i]
  * (d_i = 3072, d_m = 2048, d_out = n_q * d_k = 2048 for SIGMA-1.5B).  For
  * decode, q [M][d_out] is the query tensor [B][n_q][d_k] that diffqkv_decode
- * takes.  d_m and d_i multiples of 1024, d_out a multiple of 16.  workspace:
- * augq_workspace bytes (M * d_i bf16), 16-byte aligned.  Two kernels on
- * `stream`.
+ * takes.  d_m and d_i multiples of 1024, d_out a multiple of 16; h, the
+ * packed weights and q 16-byte aligned.  workspace: augq_workspace bytes
+ * (M * d_i bf16), 16-byte aligned.  Two kernels on `stream`.
  *
  * augq_pack -- one-time weight layout change for augq_forward: w [n_out][n_in]
  * (bf16, row-major) -> w_packed [n_out / 16][n_in / 32][64][8], element

@@ -263,7 +263,7 @@ def test_augq_validation(lib):
                                 a["wd"], a["q"], a["ws"], a["ws_bytes"], None)
     assert call(M=-1) == SHAPE and call(d_out=0) == SHAPE
     assert call(d_m=1000) == UNSUP and call(d_i=3000) == UNSUP and call(d_out=100) == UNSUP
-    assert call(wd=None) == NULL and call(h=FAKE + 2) == ALIGN
+    assert call(wd=None) == NULL and call(h=FAKE + 2) == ALIGN and call(q=FAKE + 8) == ALIGN
     assert call(ws_bytes=4 * 3072 * 2 - 1) == WS
     assert call(M=0) == OK
     size = ctypes.c_size_t()
