@@ -125,20 +125,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   // Fused append: the sequence's newest row (L - 1) is the last row of the
   // chunk that owns it.  Every wave of that chunk stores the row of its own K
   // head and V head into the cache (waves sharing a head store identical
-  // bytes), waits for its stores to complete, and then reads the row back
-  // like any other.  Only this chunk touches row L - 1.
+  // bytes) and then reads it back like any other row.  The lanes that store
+  // a 16-byte slice are exactly the lanes that later load it (the row's lane
+  // group in the K and V load patterns), so each lane reads back its own
+  // store: program order, with kc / kc_w and vc / vc_w possibly aliasing as
+  // far as the compiler knows.  Only this chunk touches row L - 1.
   if (k_new != nullptr && L - 1 - j0 < rows) {
     const int r_new = L - 1 - j0;
     const int t_new0 = r_new & ~63;  // tile holding the new row
     const size_t pg = PAGED ? page_of(t_new0) : 0;
     const int in_tile = r_new - t_new0;
-    if (lane < LPR_K)
+    if (kr == in_tile % RPL_K)
       *reinterpret_cast<u32x4*>(k_tile(kc_w, t_new0, pg) + (size_t)in_tile * DK) =
           load16(k_new + ((size_t)b * n_k + hk) * DK + kl * EPL);
-    if (lane < LPR_V)
+    if (vr == in_tile % RPL_V)
       *reinterpret_cast<u32x4*>(v_tile(vc_w, t_new0, pg) + (size_t)in_tile * DV) =
           load16(v_new + ((size_t)b * n_v + hv) * DV + vl * EPL);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // s_waitcnt on the stores
   }
 
   // The lane keeps the score of tile row my_row = kl * RPL_K + kr (K load kl,
