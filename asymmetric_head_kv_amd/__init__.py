@@ -23,7 +23,7 @@ import torch
 __all__ = ["DQKVError", "lib_path", "load", "decode", "decode_chunk",
            "decode_workspace_bytes", "decode_selective", "selective_workspace_bytes",
            "decode_paged", "kv_append_paged", "kv_group_sharing", "augq", "augq_pack",
-           "prefill", "prefill_workspace_bytes", "kv_append", "STATUS"]
+           "prefill", "prefill_paged", "prefill_workspace_bytes", "kv_append", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libdiffqkv.so")
@@ -44,6 +44,7 @@ SIGNATURES = {
     "diffqkv_decode": (_i32, [_i32] * 9 + [_f32] + [_vp] * 6 + [_i32, _vp, _sz, _vp]),
     "diffqkv_prefill": (_i32, [_i32] * 9 + [_f32] + [_vp] * 7 + [_sz, _vp]),
     "diffqkv_prefill_workspace": (_i32, [_i32] * 7 + [ctypes.POINTER(_sz)]),
+    "diffqkv_prefill_paged": (_i32, [_i32] * 11 + [_f32] + [_vp] * 8 + [_sz, _vp]),
     "diffqkv_decode_split": (_i32, [_i32] * 9 + [_f32] + [_vp] * 6 + [_i32, _vp, _sz, _vp]),
     "diffqkv_decode_append": (_i32, [_i32] * 9 + [_f32] + [_vp] * 8 + [_i32, _vp, _sz, _vp]),
     "diffqkv_decode_combine": (_i32, [_i32] * 9 + [_vp] * 3 + [_i32, _vp, _sz, _vp]),
@@ -445,4 +446,38 @@ def prefill(q, k_cache, v_cache, ctx_len, *, scale=None, out=None, lse=None,
           n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, T, l_cap, scale,
           _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(out), _ptr(lse),
           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
+    return out, lse
+
+
+
+def prefill_paged(q, k_pages, v_pages, block_table, ctx_len, *, scale=None, out=None,
+                  lse=None, workspace=None, stream=None):
+    """prefill() over a paged cache (k_pages [N, n_k, P, d_k], v_pages
+    [N, n_v, P, d_v], block_table int32 [B, max_blocks]); bit-identical to
+    prefill() on the equivalent contiguous cache."""
+    dev = _device_tensors(q, k_pages, v_pages, block_table, ctx_len, out, lse, workspace)
+    B, T, n_q, d_k = q.shape
+    num_pages, n_k, P, d_k2, n_v, d_v, max_blocks = _pages_shape(k_pages, v_pages,
+                                                                 block_table, B)
+    if d_k2 != d_k:
+        raise ValueError("q and k_pages disagree on d_k")
+    if ctx_len.dtype != torch.int32 or ctx_len.numel() != B:
+        raise ValueError("ctx_len must be int32 [B]")
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("q and the page pools must share one dtype")
+    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, T, n_q, d_v), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, T, n_q, d_v) or out.dtype != q.dtype:
+        raise ValueError("out must be [B, t_new, n_q, d_v] in q's dtype")
+    if lse is not None and (lse.shape != (B, T, n_q) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, t_new, n_q]")
+    if workspace is None:
+        need = prefill_workspace_bytes(n_q, n_k, n_v, d_k, d_v, B, T)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _call(dev, "diffqkv_prefill_paged",
+          n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, T, P, num_pages, max_blocks, scale,
+          _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_len), _ptr(out),
+          _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+          _stream(stream, dev))
     return out, lse

@@ -348,12 +348,17 @@ int32_t diffqkv_prefill_workspace(int32_t n_q, int32_t n_k, int32_t n_v, int32_t
   return DQKV_OK;
 }
 
-int32_t diffqkv_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
-                        int32_t dtype, int32_t batch, int32_t t_new, int32_t l_cap,
-                        float scale, const void* q, const void* k_cache,
-                        const void* v_cache, const int32_t* ctx_len, void* out,
-                        float* lse, void* workspace, size_t workspace_bytes_given,
-                        void* stream) {
+static int check_pages(int32_t page_rows, int32_t num_pages, int32_t max_blocks,
+                       const int32_t* table, dqkv::PageMap* pm, int* cap);
+
+// Shared by diffqkv_prefill and diffqkv_prefill_paged: validates the call
+// and launches the prefill (and, when split, its merge).  pm.table == NULL
+// means contiguous caches of l_cap rows.
+static int run_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                       int32_t dtype, int32_t batch, int32_t t_new, int32_t l_cap, float scale,
+                       const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* ctx_len, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes_given, void* stream, const dqkv::PageMap& pm) {
   int st = check_heads(n_q, n_k, n_v, d_k, d_v);
   if (st) return st;
   if (dtype != DQKV_BF16) return DQKV_ERR_UNSUPPORTED;
@@ -380,8 +385,36 @@ int32_t diffqkv_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int3
   a.part_o = ns > 1 ? (float*)workspace : nullptr;
   a.part_ml = ns > 1 ? (float*)((char*)workspace + align256((size_t)ns * rows * d_v * sizeof(float)))
                      : nullptr;
+  a.pages = pm;
   a.stream = (hipStream_t)stream;
   return to_status(dqkv::launch_prefill(a));
+}
+
+int32_t diffqkv_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                        int32_t dtype, int32_t batch, int32_t t_new, int32_t l_cap,
+                        float scale, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* ctx_len, void* out,
+                        float* lse, void* workspace, size_t workspace_bytes_given,
+                        void* stream) {
+  return run_prefill(n_q, n_k, n_v, d_k, d_v, dtype, batch, t_new, l_cap, scale, q, k_cache,
+                     v_cache, ctx_len, out, lse, workspace, workspace_bytes_given, stream,
+                     dqkv::PageMap{});
+}
+
+int32_t diffqkv_prefill_paged(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                              int32_t dtype, int32_t batch, int32_t t_new, int32_t page_rows,
+                              int32_t num_pages, int32_t max_blocks, float scale,
+                              const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, const int32_t* ctx_len, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes_given,
+                              void* stream) {
+  dqkv::PageMap pm;
+  int cap = 0;
+  int st = check_pages(page_rows, num_pages, max_blocks, block_table, &pm, &cap);
+  if (st) return st;
+  if (batch > 0 && t_new > 0 && !block_table) return DQKV_ERR_NULL;
+  return run_prefill(n_q, n_k, n_v, d_k, d_v, dtype, batch, t_new, cap, scale, q, k_pages,
+                     v_pages, ctx_len, out, lse, workspace, workspace_bytes_given, stream, pm);
 }
 
 int32_t diffqkv_decode_selective_workspace(int32_t n_q, int32_t n_k, int32_t n_v,

@@ -76,6 +76,7 @@ struct PrefillArgs {
   int n_split;      // key splits (1: no merge, no workspace)
   float* part_o;    // [n_split][B][t_new][n_q][d_v] fp32
   float* part_ml;   // [n_split][B][t_new][n_q] split lse, log2 units
+  PageMap pages;    // table == nullptr: contiguous caches
   hipStream_t stream;
 };
 

@@ -83,12 +83,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
 // lse); otherwise they add the bf16-rounded weights that the P.V product
 // multiplies, two per v_dot2_f32_bf16, which normalises O by exactly the
 // weights it used.
-template <int DK, int DV, bool kExactSum>
+//
+// PAGED: kc / vc are page pools ([num_pages][n_k][page_rows][d_k] and
+// [num_pages][n_v][page_rows][d_v]) and key row j of sequence b sits in page
+// pm.table[b][j / page_rows]; pages hold a power-of-two multiple of 64 rows,
+// so each 64-row tile lies in one page and costs one table read.  l_cap is
+// then the table's row capacity.
+template <int DK, int DV, bool kExactSum, bool PAGED>
 __global__ __launch_bounds__(256) void prefill_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     const int32_t* __restrict__ ctx_len, bf16* __restrict__ out, float* __restrict__ lse,
     int n_q, int n_k, int n_v, int t_new, int l_cap, int n_qtiles, float qscale,
-    int n_split, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    int n_split, float* __restrict__ part_o, float* __restrict__ part_ml, PageMap pm) {
   using Lds = PfLds<DK, DV>;
   constexpr int KS = DK / 16;       // 16-wide d_k steps of S^T
   constexpr int NB = DV / 32;       // 32-wide d_v blocks of O^T
@@ -135,8 +141,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       qb[s] = as_bf16x8(q_ok ? load16(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u});
   }
 
-  const bf16* kbase = kc + ((size_t)b * n_k + hk) * l_cap * DK;
-  const bf16* vbase = vc + ((size_t)b * n_v + hv) * l_cap * DV;
+  // Row j of this head's K (V) is at k_head(j) + (j % rows_per_base) * DK.
+  // Contiguous: one base for the sequence; paged: the base of j's page.
+  auto k_head = [&](int j0) -> const bf16* {
+    if constexpr (PAGED) {
+      const int blk = pm.table[(size_t)b * pm.max_blocks + (j0 >> pm.page_shift)];
+      const size_t page = (size_t)min(max(blk, 0), pm.num_pages - 1);
+      return kc + ((page * n_k + hk) << pm.page_shift) * DK;
+    }
+    return kc + ((size_t)b * n_k + hk) * l_cap * DK;
+  };
+  auto v_head = [&](int j0) -> const bf16* {
+    if constexpr (PAGED) {
+      const int blk = pm.table[(size_t)b * pm.max_blocks + (j0 >> pm.page_shift)];
+      const size_t page = (size_t)min(max(blk, 0), pm.num_pages - 1);
+      return vc + ((page * n_v + hv) << pm.page_shift) * DV;
+    }
+    return vc + ((size_t)b * n_v + hv) * l_cap * DV;
+  };
+  const int row_mask = PAGED ? (1 << pm.page_shift) - 1 : 0x7fffffff;
 
   // Tile loads, HBM -> LDS: per round the workgroup's 256 lanes fill 256
   // consecutive 16-byte slots (wave w: slots 64w .. 64w+63, in lane order).
@@ -163,23 +186,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   // row: the loads stay in bounds and every score they feed is masked.
   auto issue_k = [&](int t, int stage) {
     const int j0 = t * kPfKeys;
+    const bf16* kbase = k_head(j0);
     unsigned char* kl = lds + stage * Lds::kStage + wave_u * 1024;
     const bool full = j0 + kPfKeys <= n_keys;
 #pragma unroll
     for (int r = 0; r < KR; ++r) {
       const int j = full ? j0 + k_row[r] : min(j0 + k_row[r], n_keys - 1);
-      __builtin_amdgcn_global_load_lds(kbase + (uint32_t)(j * DK + k_off[r]),
+      __builtin_amdgcn_global_load_lds(kbase + (uint32_t)((j & row_mask) * DK + k_off[r]),
                                        (lds_void*)(kl + r * 4096), 16, 0, 0);
     }
   };
   auto issue_v = [&](int t, int stage) {
     const int j0 = t * kPfKeys;
+    const bf16* vbase = v_head(j0);
     unsigned char* vl = lds + stage * Lds::kStage + Lds::kKBytes + wave_u * 1024;
     const bool full = j0 + kPfKeys <= n_keys;
 #pragma unroll
     for (int r = 0; r < VR; ++r) {
       const int j = full ? j0 + v_row[r] : min(j0 + v_row[r], n_keys - 1);
-      __builtin_amdgcn_global_load_lds(vbase + (uint32_t)(j * DV + v_off[r]),
+      __builtin_amdgcn_global_load_lds(vbase + (uint32_t)((j & row_mask) * DV + v_off[r]),
                                        (lds_void*)(vl + r * 4096), 16, 0, 0);
     }
   };
@@ -449,21 +474,23 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
     lse[row] = wsum > 0.f ? (mx + fast_log2(wsum)) * kLn2 : -INFINITY;
 }
 
+template <int DK, int DV, bool kExact, bool PAGED>
+static void launch_prefill_kernel(const PrefillArgs& a, int n_qtiles) {
+  dim3 grid(n_qtiles * a.n_q * a.n_split, a.batch);
+  constexpr size_t lds = PfLds<DK, DV>::kTotal;
+  static_assert(lds <= 65536, "dynamic LDS above 64 KiB is not launched");
+  hipLaunchKernelGGL((prefill_kernel<DK, DV, kExact, PAGED>), grid, dim3(256), lds, a.stream,
+                     (const bf16*)a.q,
+                     (const bf16*)a.k_cache, (const bf16*)a.v_cache, a.ctx_len, (bf16*)a.out,
+                     a.lse, a.n_q, a.n_k, a.n_v, a.t_new, a.l_cap, n_qtiles,
+                     a.scale * kLog2e, a.n_split, a.part_o, a.part_ml, a.pages);
+}
+
 template <int DK, int DV, bool kExact>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
   const int n_qtiles = (a.t_new + kPfRows - 1) / kPfRows;
-  dim3 grid(n_qtiles * a.n_q * a.n_split, a.batch);
-  const size_t lds = PfLds<DK, DV>::kTotal;
-  if (lds > 65536) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_kernel<DK, DV, kExact>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (attr != hipSuccess) return attr;
-  }
-  hipLaunchKernelGGL((prefill_kernel<DK, DV, kExact>), grid, dim3(256), lds, a.stream,
-                     (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache,
-                     a.ctx_len, (bf16*)a.out, a.lse, a.n_q, a.n_k, a.n_v, a.t_new, a.l_cap,
-                     n_qtiles, a.scale * kLog2e, a.n_split, a.part_o, a.part_ml);
+  if (a.pages.table != nullptr) launch_prefill_kernel<DK, DV, kExact, true>(a, n_qtiles);
+  else launch_prefill_kernel<DK, DV, kExact, false>(a, n_qtiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.n_split == 1) return err;
   const size_t rows_total = (size_t)a.batch * a.t_new * a.n_q;

@@ -215,6 +215,27 @@ int32_t diffqkv_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
                         size_t workspace_bytes, void* stream);
 
 /*
+ * diffqkv_prefill_paged -- diffqkv_prefill over a paged cache (the page
+ * layout of diffqkv_decode_paged: k_pages [num_pages][n_k][page_rows][d_k],
+ * v_pages [num_pages][n_v][page_rows][d_v], key row j of sequence b in page
+ * block_table[b][j / page_rows], page_rows a power of two >= 64).  The row
+ * capacity max_blocks * page_rows takes the place of l_cap; entries of
+ * block_table outside [0, num_pages) are clamped (memory-safe, the result
+ * then reads another page).  Same workspace (diffqkv_prefill_workspace) and
+ * the same result, bit for bit, as diffqkv_prefill on the equivalent
+ * contiguous cache.  Not described by the pages (a layout choice; vLLM's
+ * paged attention is the prior art they name).
+ */
+int32_t diffqkv_prefill_paged(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                              int32_t d_v, int32_t dtype, int32_t batch,
+                              int32_t t_new, int32_t page_rows, int32_t num_pages,
+                              int32_t max_blocks, float scale, const void* q,
+                              const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, const int32_t* ctx_len,
+                              void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * diffqkv_decode_selective -- decode with selective V fetching (architecture
  * page, section "Selective V Cache Fetching"; a NEXT-step inference
  * optimisation, not part of the Sigma model itself).

@@ -242,6 +242,20 @@ def test_paged_and_compat_validation(lib):
     assert app(tab=None) == NULL and app(vp=FAKE + 4) == ALIGN
     assert app(T=0) == OK and app(d_k=40) == UNSUP
 
+    def pre(**kw):
+        a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=1, T=64, P=64, N=16, MB=16,
+                 scale=0.125, q=FAKE, kp=FAKE, vp=FAKE, tab=FAKE, ctx=FAKE, out=FAKE, lse=None,
+                 ws=None, ws_bytes=0)
+        a.update(kw)
+        return lib.diffqkv_prefill_paged(
+            a["n_q"], a["n_k"], a["n_v"], a["d_k"], a["d_v"], a["dtype"], a["B"], a["T"], a["P"],
+            a["N"], a["MB"], a["scale"], a["q"], a["kp"], a["vp"], a["tab"], a["ctx"], a["out"],
+            a["lse"], a["ws"], a["ws_bytes"], None)
+    assert pre(P=96) == SHAPE and pre(N=0) == SHAPE and pre(MB=0) == SHAPE
+    assert pre(tab=None) == NULL and pre(q=None) == NULL
+    assert pre(vp=FAKE + 8) == ALIGN and pre(dtype=0) == UNSUP and pre(d_k=32) == UNSUP
+    assert pre(scale=0.0) == SHAPE and pre(T=0) == OK and pre(B=0, tab=None) == OK
+
     def grp(**kw):
         a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=1, cap=256, k=FAKE,
                  v=FAKE, ko=FAKE, vo=FAKE)
