@@ -22,7 +22,7 @@ import torch
 
 __all__ = ["DQKVError", "lib_path", "load", "decode", "decode_chunk",
            "decode_workspace_bytes", "decode_selective", "selective_workspace_bytes",
-           "decode_paged", "kv_append_paged", "kv_group_sharing", "augq", "augq_pack",
+           "decode_paged", "decode_selective_paged", "kv_append_paged", "kv_group_sharing", "augq", "augq_pack",
            "prefill", "prefill_paged", "prefill_workspace_bytes", "kv_append", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -50,6 +50,7 @@ SIGNATURES = {
     "diffqkv_decode_combine": (_i32, [_i32] * 9 + [_vp] * 3 + [_i32, _vp, _sz, _vp]),
     "diffqkv_decode_selective_workspace": (_i32, [_i32] * 8 + [ctypes.POINTER(_sz)]),
     "diffqkv_decode_selective": (_i32, [_i32] * 9 + [_f32, _i32] + [_vp] * 10 + [_sz, _vp]),
+    "diffqkv_decode_selective_paged": (_i32, [_i32] * 11 + [_f32, _i32] + [_vp] * 11 + [_sz, _vp]),
     "kv_append_paged": (_i32, [_i32] * 11 + [_vp] * 7),
     "diffqkv_decode_paged": (_i32, [_i32] * 11 + [_f32] + [_vp] * 9 + [_i32, _vp, _sz, _vp]),
     "kv_group_sharing": (_i32, [_i32] * 8 + [_vp] * 5),
@@ -481,3 +482,47 @@ def prefill_paged(q, k_pages, v_pages, block_table, ctx_len, *, scale=None, out=
           _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
           _stream(stream, dev))
     return out, lse
+
+
+
+def decode_selective_paged(q, k_pages, v_pages, block_table, ctx_len, *, top_k=100,
+                           max_ctx=None, scale=None, out=None, lse=None, sel_idx=None,
+                           workspace=None, k_new=None, v_new=None, stream=None):
+    """decode_selective() over a paged cache (k_pages [N, n_k, P, d_k],
+    v_pages [N, n_v, P, d_v], block_table int32 [B, max_blocks])."""
+    dev = _device_tensors(q, k_pages, v_pages, block_table, ctx_len, out, lse, sel_idx,
+                          workspace, k_new, v_new)
+    B, n_q, d_k = q.shape
+    num_pages, n_k, P, d_k2, n_v, d_v, max_blocks = _pages_shape(k_pages, v_pages,
+                                                                 block_table, B)
+    if d_k2 != d_k:
+        raise ValueError("q and k_pages disagree on d_k")
+    if ctx_len.dtype != torch.int32 or ctx_len.numel() != B:
+        raise ValueError("ctx_len must be int32 [B]")
+    for t in (k_pages, v_pages, k_new, v_new):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError("q, the page pools and the new rows must share one dtype")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None and (k_new.numel() != B * n_k * d_k or v_new.numel() != B * n_v * d_v):
+        raise ValueError("k_new must hold [B, n_k, d_k] and v_new [B, n_v, d_v]")
+    max_ctx = max_blocks * P if max_ctx is None else int(max_ctx)
+    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    top_k = int(top_k)
+    if out is None:
+        out = torch.empty((B, n_q, d_v), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, n_q, d_v) or out.dtype != q.dtype:
+        raise ValueError("out must be [B, n_q, d_v] in q's dtype")
+    if lse is not None and (lse.shape != (B, n_q) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, n_q]")
+    if sel_idx is not None and (sel_idx.shape != (B, n_q, top_k) or sel_idx.dtype != torch.int32):
+        raise ValueError("sel_idx must be int32 [B, n_q, top_k]")
+    if workspace is None:
+        need = selective_workspace_bytes(n_q, n_k, n_v, d_k, d_v, B, max_ctx, top_k)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _call(dev, "diffqkv_decode_selective_paged",
+          n_q, n_k, n_v, d_k, d_v, _dtype_code(q), B, P, num_pages, max_blocks, max_ctx, scale,
+          top_k, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages),
+          _ptr(block_table), _ptr(ctx_len), _ptr(out), _ptr(lse), _ptr(sel_idx),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, dev))
+    return out, lse, sel_idx

@@ -431,13 +431,15 @@ int32_t diffqkv_decode_selective_workspace(int32_t n_q, int32_t n_k, int32_t n_v
   return DQKV_OK;
 }
 
-int32_t diffqkv_decode_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
-                                 int32_t d_v, int32_t dtype, int32_t batch, int32_t l_cap,
-                                 int32_t max_ctx, float scale, int32_t top_k, const void* q,
-                                 const void* k_new, const void* v_new, void* k_cache,
-                                 void* v_cache, const int32_t* ctx_len, void* out, float* lse,
-                                 int32_t* sel_idx, void* workspace,
-                                 size_t workspace_bytes_given, void* stream) {
+// Shared by diffqkv_decode_selective and its paged form (pm.table != NULL:
+// k_cache / v_cache are page pools and l_cap their table's row capacity).
+static int run_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
+                         int32_t dtype, int32_t batch, int32_t l_cap, int32_t max_ctx,
+                         float scale, int32_t top_k, const void* q, const void* k_new,
+                         const void* v_new, void* k_cache, void* v_cache,
+                         const int32_t* ctx_len, void* out, float* lse, int32_t* sel_idx,
+                         void* workspace, size_t workspace_bytes_given, void* stream,
+                         const dqkv::PageMap& pm) {
   int st = check_heads(n_q, n_k, n_v, d_k, d_v);
   if (st) return st;
   st = check_dtype_dims(dtype, d_k, d_v);
@@ -470,8 +472,38 @@ int32_t diffqkv_decode_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t 
   a.cand_s = (float*)(ws + lay.off_cs);
   a.cand_i = (int32_t*)(ws + lay.off_ci);
   a.k_new = k_new; a.v_new = v_new;
+  a.pages = pm;
   a.stream = (hipStream_t)stream;
   return to_status(dqkv::launch_decode_selective(a));
+}
+
+int32_t diffqkv_decode_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                                 int32_t d_v, int32_t dtype, int32_t batch, int32_t l_cap,
+                                 int32_t max_ctx, float scale, int32_t top_k, const void* q,
+                                 const void* k_new, const void* v_new, void* k_cache,
+                                 void* v_cache, const int32_t* ctx_len, void* out, float* lse,
+                                 int32_t* sel_idx, void* workspace,
+                                 size_t workspace_bytes_given, void* stream) {
+  return run_selective(n_q, n_k, n_v, d_k, d_v, dtype, batch, l_cap, max_ctx, scale, top_k, q,
+                       k_new, v_new, k_cache, v_cache, ctx_len, out, lse, sel_idx, workspace,
+                       workspace_bytes_given, stream, dqkv::PageMap{});
+}
+
+int32_t diffqkv_decode_selective_paged(
+    int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v, int32_t dtype,
+    int32_t batch, int32_t page_rows, int32_t num_pages, int32_t max_blocks, int32_t max_ctx,
+    float scale, int32_t top_k, const void* q, const void* k_new, const void* v_new,
+    void* k_pages, void* v_pages, const int32_t* block_table, const int32_t* ctx_len,
+    void* out, float* lse, int32_t* sel_idx, void* workspace, size_t workspace_bytes_given,
+    void* stream) {
+  dqkv::PageMap pm;
+  int cap = 0;
+  int st = check_pages(page_rows, num_pages, max_blocks, block_table, &pm, &cap);
+  if (st) return st;
+  if (batch > 0 && !block_table) return DQKV_ERR_NULL;
+  return run_selective(n_q, n_k, n_v, d_k, d_v, dtype, batch, cap, max_ctx, scale, top_k, q,
+                       k_new, v_new, k_pages, v_pages, ctx_len, out, lse, sel_idx, workspace,
+                       workspace_bytes_given, stream, pm);
 }
 
 // ---------------------------------------------------------------- paged cache

@@ -106,6 +106,7 @@ struct SelectiveArgs {
   int32_t* cand_i;    // [B][n_q][n_ranges][top_k]
   const void* k_new;  // fused append, or null
   const void* v_new;
+  PageMap pages;    // table == nullptr: contiguous caches
   hipStream_t stream;
 };
 

@@ -38,6 +38,22 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Row j of head h of sequence b: in a contiguous [B][H][l_cap][D] cache, or
+// (pm.table set) in a page pool [num_pages][H][page_rows][D] through the
+// page table, entries outside [0, num_pages) clamped.  A 64-row tile that
+// starts at a multiple of 64 lies in one page, so rows j .. j + 63 follow
+// the returned address contiguously.
+template <typename T, int D>
+__device__ __forceinline__ T* cache_row(T* c, const PageMap& pm, int b, int H, int h,
+                                        int l_cap, int j) {
+  if (pm.table != nullptr) {
+    const int blk = pm.table[(size_t)b * pm.max_blocks + (j >> pm.page_shift)];
+    const size_t page = (size_t)min(max(blk, 0), pm.num_pages - 1);
+    return c + (((page * H + h) << pm.page_shift) + (j & ((1 << pm.page_shift) - 1))) * D;
+  }
+  return c + (((size_t)b * H + h) * l_cap + j) * D;
+}
+
 __device__ __forceinline__ uint64_t lanes_below() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -283,7 +299,7 @@ template <typename T, int DK, int HW>
 __global__ __launch_bounds__(256) void sel_score_kernel(
     const T* __restrict__ q, const T* kc, const int32_t* __restrict__ ctx_len,
     float* __restrict__ scores, int n_q, int n_k, int l_cap, int max_ctx, int ld_s, int S,
-    float qscale, const T* __restrict__ k_new, T* kc_w) {
+    float qscale, const T* __restrict__ k_new, T* kc_w, PageMap pm) {
   constexpr int EPL = Elem<T>::kPer16;
   constexpr int LPR_K = DK / EPL;   // lanes per K row
   constexpr int RPL_K = 64 / LPR_K; // K rows per wave load
@@ -310,22 +326,23 @@ __global__ __launch_bounds__(256) void sel_score_kernel(
     for (int e = 0; e < EPL; ++e) qf[h][e] *= qscale;
   }
 
-  const T* kp = kc + (((size_t)b * n_k + hk) * l_cap + j0) * DK + kl * EPL;
   const bool fused = k_new != nullptr;
   const int r_new = fused ? L - 1 - j0 : -1;  // in [0, rows) iff this chunk owns it
   const T* kn = fused ? k_new + ((size_t)b * n_k + hk) * DK + kl * EPL : nullptr;
   if (fused && r_new < rows && slice == 0 && wave == (r_new / 64) % 4 && lane < LPR_K)
-    *reinterpret_cast<u32x4*>(kc_w + (((size_t)b * n_k + hk) * l_cap + L - 1) * DK + kl * EPL) =
-        load16(kn);
+    *reinterpret_cast<u32x4*>(cache_row<T, DK>(kc_w, pm, b, n_k, hk, l_cap, L - 1) +
+                              kl * EPL) = load16(kn);
 
   float* out = scores + ((size_t)b * n_q + i0) * ld_s + j0;
   const int my_row = kl * RPL_K + kr;
   for (int t0 = wave * 64; t0 < rows; t0 += 256) {
+    const T* kt = cache_row<const T, DK>(kc, pm, b, n_k, hk, l_cap, j0 + t0) + kl * EPL;
     u32x4 kv[NK];
 #pragma unroll
     for (int u = 0; u < NK; ++u) {
       const int r = t0 + u * RPL_K + kr;
-      kv[u] = r >= rows ? u32x4{0u, 0u, 0u, 0u} : load16(r == r_new ? kn : kp + (size_t)r * DK);
+      kv[u] = r >= rows ? u32x4{0u, 0u, 0u, 0u}
+                        : load16(r == r_new ? kn : kt + (size_t)(r - t0) * DK);
     }
     float s_mine[HW];
 #pragma unroll
@@ -365,7 +382,7 @@ template <int DK>
 __global__ __launch_bounds__(256) void sel_score_mfma_kernel(
     const bf16* __restrict__ q, const bf16* kc, const int32_t* __restrict__ ctx_len,
     float* __restrict__ scores, int n_q, int n_k, int l_cap, int max_ctx, int ld_s, int S,
-    float qscale, const bf16* __restrict__ k_new, bf16* kc_w) {
+    float qscale, const bf16* __restrict__ k_new, bf16* kc_w, PageMap pm) {
   constexpr int KB = DK / 32;  // k blocks per row
   const int c = blockIdx.x, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -387,16 +404,16 @@ __global__ __launch_bounds__(256) void sel_score_mfma_kernel(
         sel_bf16x8, l16 < nh ? load16(q + ((size_t)b * n_q + i0 + l16) * DK + kb * 32 + 8 * kg)
                              : u32x4{0u, 0u, 0u, 0u});
 
-  const bf16* kp = kc + (((size_t)b * n_k + hk) * l_cap + j0) * DK + 8 * kg;
   const bool fused = k_new != nullptr;
   const int r_new = fused ? L - 1 - j0 : -1;  // in [0, rows) iff this chunk owns it
   const bf16* kn = fused ? k_new + ((size_t)b * n_k + hk) * DK + 8 * kg : nullptr;
   if (fused && r_new < rows && slice == 0 && wave == (r_new / 64) % 4 && lane < DK / 8)
-    *reinterpret_cast<u32x4*>(kc_w + (((size_t)b * n_k + hk) * l_cap + L - 1) * DK + 8 * lane) =
-        load16(k_new + ((size_t)b * n_k + hk) * DK + 8 * lane);
+    *reinterpret_cast<u32x4*>(cache_row<bf16, DK>(kc_w, pm, b, n_k, hk, l_cap, L - 1) +
+                              8 * lane) = load16(k_new + ((size_t)b * n_k + hk) * DK + 8 * lane);
 
   float* out = scores + ((size_t)b * n_q + i0 + l16) * ld_s + j0;
   for (int t0 = wave * 64; t0 < rows; t0 += 256) {
+    const bf16* kt = cache_row<const bf16, DK>(kc, pm, b, n_k, hk, l_cap, j0 + t0) + 8 * kg;
     u32x4 kv[4][KB];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -404,7 +421,7 @@ __global__ __launch_bounds__(256) void sel_score_mfma_kernel(
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
         kv[rb][kb] = r >= rows ? u32x4{0u, 0u, 0u, 0u}
-                               : load16((r == r_new ? kn : kp + (size_t)r * DK) + kb * 32);
+                               : load16((r == r_new ? kn : kt + (size_t)(r - t0) * DK) + kb * 32);
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -510,7 +527,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
     const T* vc, const int32_t* __restrict__ ctx_len, const float* __restrict__ range_ml,
     const float* __restrict__ cand_s, const int32_t* __restrict__ cand_i, T* __restrict__ out,
     float* __restrict__ lse, int32_t* __restrict__ sel_idx, int n_q, int n_v, int l_cap,
-    int max_ctx, int n_ranges, int top_k, const T* __restrict__ v_new, T* vc_w) {
+    int max_ctx, int n_ranges, int top_k, const T* __restrict__ v_new, T* vc_w, PageMap pm) {
   constexpr int EPL = Elem<T>::kPer16;
   constexpr int LPR = DV / EPL;               // lanes per V row
   constexpr int RPP = kSelThreads / LPR;      // V rows per pass of the block
@@ -530,8 +547,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
   const bool fused = v_new != nullptr;
   const T* vn = fused ? v_new + ((size_t)b * n_v + hv) * DV : nullptr;
   if (fused && L > 0 && i % (n_q / n_v) == 0 && tid < LPR)
-    *reinterpret_cast<u32x4*>(vc_w + (((size_t)b * n_v + hv) * l_cap + L - 1) * DV + tid * EPL) =
-        load16(vn + tid * EPL);
+    *reinterpret_cast<u32x4*>(cache_row<T, DV>(vc_w, pm, b, n_v, hv, l_cap, L - 1) +
+                              tid * EPL) = load16(vn + tid * EPL);
 
   // Candidates: range r contributed min(top_k, rows of r) entries at
   // [r * top_k, ...); all ranges but the last are full, so the n_c entries
@@ -604,7 +621,6 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
   // o = sum over the selected rows of w_j V_j: LPR lanes per row, RPP rows
   // per pass, the loads of U passes issued before their use.
   const int vl = tid % LPR, vr = tid / LPR;
-  const T* vbase = vc + ((size_t)b * n_v + hv) * l_cap * DV + vl * EPL;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
@@ -619,7 +635,9 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
       if (r < kk) {
         const int j = sel_j[r];
         w[u] = sel_w[r];
-        v[u] = (fused && j == L - 1) ? load16(vn + vl * EPL) : load16(vbase + (size_t)j * DV);
+        v[u] = (fused && j == L - 1)
+                   ? load16(vn + vl * EPL)
+                   : load16(cache_row<const T, DV>(vc, pm, b, n_v, hv, l_cap, j) + vl * EPL);
       }
     }
 #pragma unroll
@@ -659,7 +677,7 @@ static hipError_t launch_score_hw(const SelectiveArgs& a) {
   hipLaunchKernelGGL((sel_score_kernel<T, DK, HW>), grid, dim3(256), 0, a.stream, (const T*)a.q,
                      (const T*)a.k_cache, a.ctx_len, a.scores, a.n_q, a.n_k, a.l_cap,
                      a.max_ctx, a.ld_s, a.S, a.scale * kLog2e, (const T*)a.k_new,
-                     (T*)a.k_cache);
+                     (T*)a.k_cache, a.pages);
   return hipGetLastError();
 }
 
@@ -684,7 +702,7 @@ static hipError_t launch_gather_t(const SelectiveArgs& a) {
   hipLaunchKernelGGL((sel_gather_kernel<T, DV>), dim3(a.n_q, a.batch), dim3(kSelThreads), 0,
                      a.stream, (const T*)a.v_cache, a.ctx_len, a.range_ml, a.cand_s, a.cand_i,
                      (T*)a.out, a.lse, a.sel_idx, a.n_q, a.n_v, a.l_cap, a.max_ctx,
-                     a.n_ranges, a.top_k, (const T*)a.v_new, (T*)a.v_cache);
+                     a.n_ranges, a.top_k, (const T*)a.v_new, (T*)a.v_cache, a.pages);
   return hipGetLastError();
 }
 
@@ -695,7 +713,7 @@ static hipError_t launch_score_mfma(const SelectiveArgs& a) {
   hipLaunchKernelGGL((sel_score_mfma_kernel<DK>), grid, dim3(256), 0, a.stream, (const bf16*)a.q,
                      (const bf16*)a.k_cache, a.ctx_len, a.scores, a.n_q, a.n_k, a.l_cap,
                      a.max_ctx, a.ld_s, a.S, a.scale * kLog2e, (const bf16*)a.k_new,
-                     (bf16*)a.k_cache);
+                     (bf16*)a.k_cache, a.pages);
   return hipGetLastError();
 }
 

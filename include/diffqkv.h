@@ -294,8 +294,8 @@ int32_t diffqkv_decode_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t 
  * two pages, so each tile costs one table read).  The row capacity of a
  * sequence is max_blocks * page_rows.  Table entries outside
  * [0, num_pages) are not followed: kv_append_paged skips such rows and the
- * decode reads page 0 in their place (a result for a malformed table, never
- * an out-of-bounds access).
+ * decode, prefill and selective paths clamp them into [0, num_pages) (a
+ * wrong result for a malformed table, never an out-of-bounds access).
  *
  * kv_append_paged -- kv_append into a paged cache (pos, t_new, k_new, v_new
  *   as for kv_append; rows past the capacity are skipped).
@@ -322,6 +322,20 @@ int32_t diffqkv_decode_paged(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
                              void* out, float* lse, int32_t chunk_tokens,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * diffqkv_decode_selective_paged -- diffqkv_decode_selective over a paged
+ * cache (the layout above).  max_ctx <= max_blocks * page_rows; the same
+ * workspace (diffqkv_decode_selective_workspace) and the same result, bit
+ * for bit, as the contiguous call on the equivalent cache.
+ */
+int32_t diffqkv_decode_selective_paged(
+    int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v, int32_t dtype,
+    int32_t batch, int32_t page_rows, int32_t num_pages, int32_t max_blocks,
+    int32_t max_ctx, float scale, int32_t top_k, const void* q, const void* k_new,
+    const void* v_new, void* k_pages, void* v_pages, const int32_t* block_table,
+    const int32_t* ctx_len, void* out, float* lse, int32_t* sel_idx, void* workspace,
+    size_t workspace_bytes, void* stream);
 
 /*
  * kv_group_sharing -- the compatibility expansion for frameworks whose

@@ -256,6 +256,21 @@ def test_paged_and_compat_validation(lib):
     assert pre(vp=FAKE + 8) == ALIGN and pre(dtype=0) == UNSUP and pre(d_k=32) == UNSUP
     assert pre(scale=0.0) == SHAPE and pre(T=0) == OK and pre(B=0, tab=None) == OK
 
+    def sel(**kw):
+        a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=1, P=64, N=16, MB=16,
+                 max_ctx=1024, scale=0.125, k=100, q=FAKE, kn=None, vn=None, kp=FAKE, vp=FAKE,
+                 tab=FAKE, ctx=FAKE, out=FAKE, lse=None, idx=None, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.diffqkv_decode_selective_paged(
+            a["n_q"], a["n_k"], a["n_v"], a["d_k"], a["d_v"], a["dtype"], a["B"], a["P"],
+            a["N"], a["MB"], a["max_ctx"], a["scale"], a["k"], a["q"], a["kn"], a["vn"],
+            a["kp"], a["vp"], a["tab"], a["ctx"], a["out"], a["lse"], a["idx"], a["ws"],
+            a["ws_bytes"], None)
+    assert sel(P=32) == SHAPE and sel(N=0) == SHAPE and sel(max_ctx=16 * 64 + 1) == SHAPE
+    assert sel(tab=None) == NULL and sel(kn=FAKE) == NULL and sel(vp=FAKE + 4) == ALIGN
+    assert sel(k=0) == SHAPE and sel(k=1025) == UNSUP and sel(ws_bytes=0) == WS
+    assert sel(B=0, tab=None) == OK
+
     def grp(**kw):
         a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=1, cap=256, k=FAKE,
                  v=FAKE, ko=FAKE, vo=FAKE)

@@ -267,3 +267,62 @@ def test_paged_prefill_matches_contiguous(P, lens, t_new):
     qw, kw, vw = case.widened()
     ref, _ = oracle.prefill(qw[:, -4:], kw, vw, case.ctx_len, case.scale)
     assert_close(to_host(out_p)[:, -4:], ref, "bf16", "paged prefill, last rows")
+
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_paged_selective_matches_contiguous(fused):
+    # Selective V over 64-row pages in a random order: the same logits, the
+    # same chosen rows and the same sums as on the contiguous cache, bit for
+    # bit; with the fused append both caches receive the same new row.
+    lens, P, top_k = [3000, 1234], 64, 100
+    B = len(lens)
+    _say("paged selective", "fused" if fused else "plain", lens)
+    case = synth.make_case(990 + fused, dtype="bf16", batch=B, n_q=16, n_k=4, n_v=16, d_k=64,
+                           d_v=128, ctx_len=lens, l_cap=max(lens))
+    q, k, v, ctx = upload(case)
+    rng = np.random.default_rng(7 + fused)
+    need = [-(-L // P) for L in lens]
+    n_pages = sum(need) + 2
+    order = rng.permutation(n_pages)
+    table = np.full((B, max(need)), -1, dtype=np.int32)
+    kp = np.zeros((n_pages, 4, P, 64), dtype=case.k_cache.dtype)
+    vp = np.zeros((n_pages, 16, P, 128), dtype=case.v_cache.dtype)
+    nxt = 0
+    for b, L in enumerate(lens):
+        for blk in range(need[b]):
+            page = int(order[nxt])
+            nxt += 1
+            table[b, blk] = page
+            r1 = min((blk + 1) * P, L)
+            kp[page, :, :r1 - blk * P] = case.k_cache[b, :, blk * P:r1]
+            vp[page, :, :r1 - blk * P] = case.v_cache[b, :, blk * P:r1]
+    kp_d, vp_d, tab_d = to_dev(kp, "bf16"), to_dev(vp, "bf16"), ints_to_dev(table)
+    kw_ = vw_ = None
+    if fused:
+        kn, vn = synth.new_rows(991, dtype="bf16", batch=B, t_new=1, n_k=4, n_v=16, d_k=64,
+                                d_v=128)
+        kw_, vw_ = to_dev(kn, "bf16"), to_dev(vn, "bf16")
+    outs = []
+    for paged in (False, True):
+        lse = torch.empty((B, 16), dtype=torch.float32, device="cuda")
+        idx = torch.empty((B, 16, top_k), dtype=torch.int32, device="cuda")
+        if paged:
+            o, _, _ = dq.decode_selective_paged(q, kp_d, vp_d, tab_d, ctx, top_k=top_k,
+                                                max_ctx=max(lens), scale=case.scale, lse=lse,
+                                                sel_idx=idx, k_new=kw_, v_new=vw_)
+        else:
+            o, _, _ = dq.decode_selective(q, k, v, ctx, top_k=top_k, scale=case.scale, lse=lse,
+                                          sel_idx=idx, k_new=kw_, v_new=vw_)
+        outs.append((o, lse, idx))
+    torch.cuda.synchronize()
+    for a, b_ in zip(outs[0], outs[1]):
+        np.testing.assert_array_equal(raw_host(a), raw_host(b_))
+    if fused:
+        # The appended rows landed in the right page slots.
+        kph, vph = raw_host(kp_d), raw_host(vp_d)
+        kh, vh = raw_host(k), raw_host(v)
+        for b, L in enumerate(lens):
+            page, slot = table[b, (L - 1) // P], (L - 1) % P
+            np.testing.assert_array_equal(kph[page, :, slot], kh[b, :, L - 1])
+            np.testing.assert_array_equal(vph[page, :, slot], vh[b, :, L - 1])
