@@ -107,3 +107,21 @@ def test_augq_tiled_rows_do_not_depend_on_the_batch():
                                   q_part.view(torch.int16).cpu().numpy())
     ref_q, _ = oracle.augq(*case.widened())
     assert_close(to_host(q_all), ref_q, "bf16", "augq 260 rows")
+
+
+
+def test_augq_full_size_sampled_rows():
+    # The SIGMA-1.5B shape at 2048 tokens, in the configuration the benchmark
+    # times (eight-wave tiled products): 24 sampled rows against the oracle
+    # (each token's query depends on that token alone).
+    sh = synth.AUGQ_SIGMA15B
+    case = synth.make_augq(7, M=2048, **sh)
+    h = to_dev(case.h, "bf16")
+    wg, wu, wd = (dq.augq_pack(to_dev(x, "bf16")) for x in (case.w_gate, case.w_up, case.w_down))
+    q = dq.augq(h, wg, wu, wd)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(5).choice(2048, size=24, replace=False)
+    hw, wgw, wuw, wdw = case.widened()
+    ref_q, _ = oracle.augq(hw[rows], wgw, wuw, wdw)
+    err = assert_close(to_host(q)[rows], ref_q, "bf16", "augq 2048 tokens, sampled rows")
+    _say(f"  normwise rel err (24 sampled rows): {err:.2e}")

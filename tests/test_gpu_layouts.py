@@ -326,3 +326,28 @@ def test_paged_selective_matches_contiguous(fused):
             page, slot = table[b, (L - 1) // P], (L - 1) % P
             np.testing.assert_array_equal(kph[page, :, slot], kh[b, :, L - 1])
             np.testing.assert_array_equal(vph[page, :, slot], vh[b, :, L - 1])
+
+
+
+def test_paged_decode_full_size_matches_contiguous():
+    # The 32k single-sequence workload in 64-row pages (a seeded random page
+    # order, as the benchmark's paged leg): bit-identical to the contiguous
+    # decode, whose full-size parity with the oracle is tested elsewhere.
+    wl = synth.workload("decode32k_asym")
+    L = int(np.asarray(wl["ctx_len"]).reshape(-1)[0])
+    case = synth.make_case(17, dtype="bf16", batch=1, n_q=16, n_k=4, n_v=16, d_k=64, d_v=128,
+                           ctx_len=[L], l_cap=L)
+    q, k, v, ctx = upload(case)
+    P = 64
+    n_pg = -(-L // P)
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(n_pg)).to("cuda")
+    kp = torch.empty((n_pg, 4, P, 64), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty((n_pg, 16, P, 128), dtype=torch.bfloat16, device="cuda")
+    kp[perm] = k[0].view(4, n_pg, P, 64).permute(1, 0, 2, 3)
+    vp[perm] = v[0].view(16, n_pg, P, 128).permute(1, 0, 2, 3)
+    table = perm.to(torch.int32).view(1, n_pg)
+    _say("paged decode, full size", L, "pages", n_pg)
+    out_p, _ = dq.decode_paged(q, kp, vp, table, ctx, max_ctx=L, scale=case.scale)
+    out_c, _ = dq.decode(q, k, v, ctx, scale=case.scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(raw_host(out_p), raw_host(out_c))
