@@ -75,6 +75,20 @@ struct PfLds {
   __device__ static int vswz(int j) { return 4 * ((j / VR256) & (V16 / 4 - 1)); }
 };
 
+// One 16-byte-per-lane HBM -> LDS transfer (global_load_lds_dwordx4): lane
+// i's 16 bytes from g land at LDS address l + 16 i, l in m0.  Issued through
+// asm because the compiler cannot tell the LDS stages apart: after the
+// builtin form it makes the first LDS read that follows wait (vmcnt 0) for
+// the transfer, which exposed the whole HBM latency of the next tile in every
+// step.  The key loop waits for these transfers itself (vmcnt 0, then the
+// barrier) before any wave reads the stage they fill; the s_nop covers the
+// one wait state a transfer needs after m0 is written.
+__device__ __forceinline__ void dma16(const void* g, lds_void* l) {
+  const uint32_t m = (uint32_t)(size_t)l;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(m) : "memory", "m0");
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -139,6 +153,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       qb[s] = as_bf16x8(q_ok ? load16(qp + 16 * s) : u32x4{0u, 0u, 0u, 0u});
+    // vmcnt(0) as a compiler-visible wait: Q is in registers before the key
+    // loop, so the compiler adds no wait for it inside the loop (where it
+    // would also wait for the in-flight tile transfers).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
   // Row j of this head's K (V) is at k_head(j) + (j % rows_per_base) * DK.
@@ -192,8 +210,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
     for (int r = 0; r < KR; ++r) {
       const int j = full ? j0 + k_row[r] : min(j0 + k_row[r], n_keys - 1);
-      __builtin_amdgcn_global_load_lds(kbase + (uint32_t)((j & row_mask) * DK + k_off[r]),
-                                       (lds_void*)(kl + r * 4096), 16, 0, 0);
+      dma16(kbase + (uint32_t)((j & row_mask) * DK + k_off[r]), (lds_void*)(kl + r * 4096));
     }
   };
   auto issue_v = [&](int t, int stage) {
@@ -204,8 +221,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
     for (int r = 0; r < VR; ++r) {
       const int j = full ? j0 + v_row[r] : min(j0 + v_row[r], n_keys - 1);
-      __builtin_amdgcn_global_load_lds(vbase + (uint32_t)((j & row_mask) * DV + v_off[r]),
-                                       (lds_void*)(vl + r * 4096), 16, 0, 0);
+      dma16(vbase + (uint32_t)((j & row_mask) * DV + v_off[r]), (lds_void*)(vl + r * 4096));
     }
   };
 
@@ -234,18 +250,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   for (int n = 0; n < NB; ++n) o[n] = f32x16{};
 
   const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
-  // S^T of one tile (K in LDS at kl) into sx: two 32-key blocks.
-  auto qk = [&](const unsigned char* kl, f32x16 (&sx)[2]) {
+  // K operands of one tile (A of S^T, 16 bytes per lane), all 2 KS reads
+  // issued together so that the S^T products never wait on one read each.
+  auto kread = [&](const unsigned char* kl, bf16x8 (&ka)[2 * KS]) {
+#pragma unroll
+    for (int u = 0; u < 2 * KS; ++u)
+      ka[u] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+          kl + (u / KS) * 32 * Lds::K16 * 16 + k_rd[u % KS]));
+  };
+  // S^T of one tile from its K operands into sx: two 32-key blocks.
+  auto qk2 = [&](const bf16x8 (&ka)[2 * KS], f32x16 (&sx)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sx[kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            kl + kb * 32 * Lds::K16 * 16 + k_rd[ks]));
-        sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], sx[kb], 0, 0, 0);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb * KS + ks], qb[ks], sx[kb], 0, 0, 0);
     }
+  };
+  auto qk = [&](const unsigned char* kl, f32x16 (&sx)[2]) {
+    bf16x8 ka[2 * KS];
+    kread(kl, ka);
+    qk2(ka, sx);
   };
   // A tile's row maximum of the scaled scores (the two lane halves of a
   // query row joined by one shuffle).
@@ -357,9 +383,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     // The three phases run at raised wave priority (back to normal before
     // the next tile's wait): measured 2.5% faster than without.
     __builtin_amdgcn_s_setprio(1);
-    qk(stage_k(nxt), sn);
+    bf16x8 ka[2 * KS];
+    kread(stage_k(nxt), ka);
+    __builtin_amdgcn_sched_barrier(0);  // the K reads go out first
+    qk2(ka, sn);
     make_p(sc, 0, pb, psum, m_use);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int k = 0; k < 2 * KS; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
