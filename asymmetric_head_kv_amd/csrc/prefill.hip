@@ -89,6 +89,19 @@ __device__ __forceinline__ void dma16(const void* g, lds_void* l) {
                :: "v"(g), "s"(m) : "memory", "m0");
 }
 
+// The same transfer from a wave-uniform base (SGPR pair) plus a per-lane
+// byte offset, so that the per-tile address arithmetic stays on the scalar
+// unit.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, lds_void* l) {
+  const uint32_t m = (uint32_t)(size_t)l;
+  const uint64_t a = (uint64_t)base;
+  const uint64_t su = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  base = (const void*)su;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(m) : "memory", "m0");
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -135,12 +148,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const int r0 = qt * kPfRows;                 // first query row of the workgroup
   const int base = L - t_new;                  // position of new row 0
   const int r_last = min(r0 + kPfRows, t_new) - 1;
-  const int n_keys = max(0, min(L, base + r_last + 1));  // keys any row here sees
+  // (Workgroup-uniform values pinned to scalar registers with readfirstlane,
+  // so that the tile bookkeeping below compiles to scalar branches.)
+  const int n_keys = __builtin_amdgcn_readfirstlane(max(0, min(L, base + r_last + 1)));
   // This workgroup's share of the key tiles: split s of n_split.
   const int all_tiles = (n_keys + kPfKeys - 1) / kPfKeys;
   const int per_split = (all_tiles + n_split - 1) / n_split;
-  const int t_begin = min(all_tiles, split * per_split);
-  const int t_end = min(all_tiles, t_begin + per_split);
+  const int t_begin = __builtin_amdgcn_readfirstlane(min(all_tiles, split * per_split));
+  const int t_end = __builtin_amdgcn_readfirstlane(min(all_tiles, t_begin + per_split));
 
   // This lane's query row and its Q^T operands (B operand: lane = q column
   // col, 8 consecutive d_k elements 8h..8h+7 of each 16-wide step).
@@ -187,41 +202,52 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   constexpr int VR = kPfKeys * Lds::V16 / 256;   // V rounds per tile
   static_assert(KR >= 1 && VR >= 1, "tile");
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  int k_row[KR], k_off[KR], v_row[VR], v_off[VR];
+  // Slot r of this lane: key row slot / row16 of the tile, logical chunk
+  // (slot % row16) ^ swizzle(row) of that row (element offset).
+  auto k_row = [&](int r) { return (r * 256 + tid) / Lds::K16; };
+  auto k_off = [&](int r) { return (((r * 256 + tid) % Lds::K16) ^ Lds::kswz(k_row(r))) * 8; };
+  auto v_row = [&](int r) { return (r * 256 + tid) / Lds::V16; };
+  auto v_off = [&](int r) { return (((r * 256 + tid) % Lds::V16) ^ Lds::vswz(v_row(r))) * 8; };
+  // Byte offsets of this lane's slots from the tile's first row (full tiles).
+  uint32_t k_vo[KR], v_vo[VR];
 #pragma unroll
-  for (int r = 0; r < KR; ++r) {
-    const int slot = r * 256 + tid;
-    k_row[r] = slot / Lds::K16;
-    k_off[r] = ((slot % Lds::K16) ^ Lds::kswz(k_row[r])) * 8;
-  }
+  for (int r = 0; r < KR; ++r) k_vo[r] = (uint32_t)(k_row(r) * DK + k_off(r)) * 2u;
 #pragma unroll
-  for (int r = 0; r < VR; ++r) {
-    const int slot = r * 256 + tid;
-    v_row[r] = slot / Lds::V16;
-    v_off[r] = ((slot % Lds::V16) ^ Lds::vswz(v_row[r])) * 8;
-  }
-  // Rows past n_keys (only in the last tile) are clamped to the last visible
-  // row: the loads stay in bounds and every score they feed is masked.
+  for (int r = 0; r < VR; ++r) v_vo[r] = (uint32_t)(v_row(r) * DV + v_off(r)) * 2u;
+  // A full tile goes from its first row's address (scalar) plus the lane
+  // offsets; in the last, partial tile rows past n_keys are clamped to the
+  // last visible row: the loads stay in bounds and every score they feed is
+  // masked.
   auto issue_k = [&](int t, int stage) {
     const int j0 = t * kPfKeys;
     const bf16* kbase = k_head(j0);
     unsigned char* kl = lds + stage * Lds::kStage + wave_u * 1024;
-    const bool full = j0 + kPfKeys <= n_keys;
+    if (j0 + kPfKeys <= n_keys) {
+      const bf16* tb = kbase + (size_t)(j0 & row_mask) * DK;
 #pragma unroll
-    for (int r = 0; r < KR; ++r) {
-      const int j = full ? j0 + k_row[r] : min(j0 + k_row[r], n_keys - 1);
-      dma16(kbase + (uint32_t)((j & row_mask) * DK + k_off[r]), (lds_void*)(kl + r * 4096));
+      for (int r = 0; r < KR; ++r) dma16s(tb, k_vo[r], (lds_void*)(kl + r * 4096));
+    } else {
+#pragma unroll
+      for (int r = 0; r < KR; ++r) {
+        const int j = min(j0 + k_row(r), n_keys - 1);
+        dma16(kbase + (uint32_t)((j & row_mask) * DK + k_off(r)), (lds_void*)(kl + r * 4096));
+      }
     }
   };
   auto issue_v = [&](int t, int stage) {
     const int j0 = t * kPfKeys;
     const bf16* vbase = v_head(j0);
     unsigned char* vl = lds + stage * Lds::kStage + Lds::kKBytes + wave_u * 1024;
-    const bool full = j0 + kPfKeys <= n_keys;
+    if (j0 + kPfKeys <= n_keys) {
+      const bf16* tb = vbase + (size_t)(j0 & row_mask) * DV;
 #pragma unroll
-    for (int r = 0; r < VR; ++r) {
-      const int j = full ? j0 + v_row[r] : min(j0 + v_row[r], n_keys - 1);
-      dma16(vbase + (uint32_t)((j & row_mask) * DV + v_off[r]), (lds_void*)(vl + r * 4096));
+      for (int r = 0; r < VR; ++r) dma16s(tb, v_vo[r], (lds_void*)(vl + r * 4096));
+    } else {
+#pragma unroll
+      for (int r = 0; r < VR; ++r) {
+        const int j = min(j0 + v_row(r), n_keys - 1);
+        dma16(vbase + (uint32_t)((j & row_mask) * DV + v_off(r)), (lds_void*)(vl + r * 4096));
+      }
     }
   };
 
@@ -314,15 +340,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     }
   };
   // P for one 32-key block: exponentials, row sums, bf16 operands.
-  auto make_p = [&](const f32x16 (&sx)[2], int kb, bf16x8 (&pb)[4], float& psum,
+  auto make_p = [&](const f32x16 (&sx)[2], int kb, bf16x8 (&pb)[4], float (&psum)[2],
                     float m_use) {
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float p0 = fast_exp2(fmaf(sx[kb][r], qscale, -m_use));
       const float p1 = fast_exp2(fmaf(sx[kb][r + 1], qscale, -m_use));
       const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-      if constexpr (kExactSum) psum += p0 + p1;
-      else psum = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnes, psum, false);
+      if constexpr (kExactSum) psum[(r >> 1) & 1] += p0 + p1;
+      else psum[(r >> 1) & 1] = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnes, psum[(r >> 1) & 1], false);
       pb[kb * 2 + (r >> 3)][r & 7] = pk[0];
       pb[kb * 2 + (r >> 3)][(r & 7) + 1] = pk[1];
     }
@@ -378,7 +404,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     if (t + 1 < t_end) issue_v(t + 1, nxt);
     rescale(m_tile);
     const float m_use = m_run == -INFINITY ? 0.f : m_run;  // rows with nothing visible yet
-    float psum = 0.f;
+    float psum[2] = {0.f, 0.f};  // two chains of row-sum additions
     bf16x8 pb[4];
     // The three phases run at raised wave priority (back to normal before
     // the next tile's wait): measured 2.5% faster than without.
@@ -404,8 +430,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads for a later MFMA
     }
-    psum += __shfl_xor(psum, 32);
-    l_run += psum;
+    float ps = psum[0] + psum[1];
+    ps += __shfl_xor(ps, 32);
+    l_run += ps;
     mask(sn, t + 1);
     pv(stage_v(cur), 2, pb);
     pv(stage_v(cur), 3, pb);
