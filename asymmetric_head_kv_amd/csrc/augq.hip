@@ -257,24 +257,28 @@ __global__ __launch_bounds__(64 * WN * WM) void augq_tiled_kernel(
     __syncthreads();
     if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
     const unsigned char* base = lds + st * STAGE + lane * 16;
+    // All operands of the stage are read first, then multiplied.
+    aq_bf16x8 wf[KB][NF], af[KB][MF];
 #pragma unroll
     for (int s = 0; s < KB; ++s) {
-      aq_bf16x8 wf[NF], af[MF];
 #pragma unroll
       for (int i = 0; i < NF; ++i)
-        wf[i] = *reinterpret_cast<const aq_bf16x8*>(base + ((wn * NF + i) * KB + s) * 1024);
+        wf[s][i] = *reinterpret_cast<const aq_bf16x8*>(base + ((wn * NF + i) * KB + s) * 1024);
 #pragma unroll
       for (int j = 0; j < MF; ++j) {
         const int r = (wm * MF + j) * 16 + (lane & 15), c = 4 * s + (lane >> 4);
-        af[j] = *reinterpret_cast<const aq_bf16x8*>(lds + st * STAGE + BFR * 1024 + r * 128 +
-                                                   ((c ^ ((r >> 1) & 7)) << 4));
+        af[s][j] = *reinterpret_cast<const aq_bf16x8*>(lds + st * STAGE + BFR * 1024 + r * 128 +
+                                                      ((c ^ ((r >> 1) & 7)) << 4));
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < KB; ++s)
 #pragma unroll
       for (int i = 0; i < NF; ++i)
 #pragma unroll
         for (int j = 0; j < MF; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s][i], af[s][j], acc[i][j], 0, 0, 0);
   }
 
   // D[n][m]: lane l holds m = l % 16 and n = 4 (l / 16) .. +3 of its block.
