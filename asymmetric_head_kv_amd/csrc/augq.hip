@@ -26,11 +26,11 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace dqkv {
 
 typedef __bf16 aq_bf16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 // W = waves splitting the reduction; STEPS = 32-wide reduction steps whose
 // loads are issued together (a wave's whole slice at decode sizes).
@@ -138,8 +138,9 @@ static hipError_t launch_gemm(const bf16* A, const bf16* B0, const bf16* B1, bf1
 // Larger M: C[M][N] = A[M][K] . B[N][K]^T with both operands staged in LDS.
 // A workgroup (4 or 8 waves) owns BN weight rows x BM activation rows and
 // walks the reduction in 64-wide stages through S LDS buffers, every load
-// going from HBM straight into LDS (16-byte global_load_lds: lane l of a
-// wave instruction fills bytes 16 l .. 16 l + 15 of a 1 KiB block).
+// going from HBM straight into LDS (16-byte global_load_lds, issued through
+// asm so that only the kernel's own waits order them: lane l of a wave
+// instruction fills bytes 16 l .. 16 l + 15 of a 1 KiB block).
 //   * Weights: one instruction = one packed 1 KiB fragment (16 rows x 32
 //     reduction elements, contiguous in the packed weights); in LDS a
 //     16-lane group reads 256 contiguous bytes per operand.
@@ -229,10 +230,7 @@ __global__ __launch_bounds__(64 * WN * WM) void augq_tiled_kernel(
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const size_t adv = is_w[u] ? (size_t)kt * KB * 512 : (size_t)kt * BK;
-      // (The untyped source pointer also keeps the host pass emitting this
-      // kernel's launch stub.)
-      __builtin_amdgcn_global_load_lds((const void*)(src[u] + adv),
-                                       (lds_void_t*)(dst + (wave + NW * u) * 1024), 16, 0, 0);
+      dma16(src[u] + adv, (lds_dma_t*)(dst + (wave + NW * u) * 1024));
     }
   };
 
@@ -243,22 +241,10 @@ __global__ __launch_bounds__(64 * WN * WM) void augq_tiled_kernel(
     for (int j = 0; j < MF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = K / BK;
-#pragma unroll
-  for (int k = 0; k < S - 1; ++k)
-    if (k < nk) issue(k, k);
-  for (int kt = 0; kt < nk; ++kt) {
+  // A wave's operands of stage kt (16-byte LDS reads into registers).
+  auto read_ops = [&](int kt, aq_bf16x8 (&wf)[KB][NF], aq_bf16x8 (&af)[KB][MF]) {
     const int st = kt % S;
-    // Stage kt has landed for this wave (the loads of the S - 2 later stages
-    // may still be in flight; near the end wait for everything), then for
-    // every wave, and every wave is done with the stage that receives stage
-    // kt + S - 1.
-    if (kt + S - 2 < nk) __builtin_amdgcn_s_waitcnt(VmWait<(S - 2) * LPW>::kImm);
-    else __builtin_amdgcn_s_waitcnt(VmWait<0>::kImm);
-    __syncthreads();
-    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
     const unsigned char* base = lds + st * STAGE + lane * 16;
-    // All operands of the stage are read first, then multiplied.
-    aq_bf16x8 wf[KB][NF], af[KB][MF];
 #pragma unroll
     for (int s = 0; s < KB; ++s) {
 #pragma unroll
@@ -271,7 +257,8 @@ __global__ __launch_bounds__(64 * WN * WM) void augq_tiled_kernel(
                                                       ((c ^ ((r >> 1) & 7)) << 4));
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mul = [&](const aq_bf16x8 (&wf)[KB][NF], const aq_bf16x8 (&af)[KB][MF]) {
 #pragma unroll
     for (int s = 0; s < KB; ++s)
 #pragma unroll
@@ -279,6 +266,24 @@ __global__ __launch_bounds__(64 * WN * WM) void augq_tiled_kernel(
 #pragma unroll
         for (int j = 0; j < MF; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s][i], af[s][j], acc[i][j], 0, 0, 0);
+  };
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k)
+    if (k < nk) issue(k, k);
+  for (int kt = 0; kt < nk; ++kt) {
+    // Stage kt has landed for this wave (the loads of the S - 2 later
+    // stages may still be in flight; near the end wait for everything),
+    // then for every wave, and every wave is done with the buffer that
+    // receives stage kt + S - 1.
+    if (kt + S - 2 < nk) __builtin_amdgcn_s_waitcnt(VmWait<(S - 2) * LPW>::kImm);
+    else __builtin_amdgcn_s_waitcnt(VmWait<0>::kImm);
+    __syncthreads();
+    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+    // All operands of the stage are read first, then multiplied.
+    aq_bf16x8 wf[KB][NF], af[KB][MF];
+    read_ops(kt, wf, af);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(wf, af);
   }
 
   // D[n][m]: lane l holds m = l % 16 and n = 4 (l / 16) .. +3 of its block.
@@ -326,7 +331,7 @@ static hipError_t launch_tiled(const bf16* A, const bf16* B0, const bf16* B1, bf
 // per workgroup (each weight load feeds four products), eight waves, four
 // steps per round.  Beyond that the LDS-tiled product: from 1024 rows eight
 // waves per workgroup on 192 x 256 gate/up tiles (96 output columns) and
-// 128 x 128 down tiles with three stages; below, four waves on 128 x 128
+// 128 x 128 down tiles with four stages; below, four waves on 128 x 128
 // gate/up tiles (64 output columns) and 64 x 128 down tiles.  Widths that
 // do not divide into whole tiles take the 64-row kernel.
 template <bool SWIGLU>
@@ -342,7 +347,7 @@ static hipError_t gemm(const bf16* A, const bf16* B0, const bf16* B1, bf16* C, i
         return launch_tiled<true, 128, 128, 2, 2, 64, 2>(A, B0, B1, C, M, N, K, stream);
     } else {
       if (big && N % 128 == 0)
-        return launch_tiled<false, 128, 128, 2, 4, 64, 3>(A, B0, B1, C, M, N, K, stream);
+        return launch_tiled<false, 128, 128, 2, 4, 64, 4>(A, B0, B1, C, M, N, K, stream);
       if (N % 64 == 0)
         return launch_tiled<false, 64, 128, 1, 4, 64, 2>(A, B0, B1, C, M, N, K, stream);
     }

@@ -1,0 +1,43 @@
+// HBM -> LDS transfers (global_load_lds_dwordx4) issued through inline asm.
+//
+// One instruction moves 16 bytes per lane: lane i's 16 bytes from its global
+// address land at LDS byte address m0 + 16 i.  The builtin form is tracked
+// by the compiler, which cannot tell apart the LDS buffers a kernel cycles
+// through: it then makes the first LDS read after a transfer, and every
+// workgroup barrier (whose release covers LDS writes), wait until all
+// transfers in flight have landed (s_waitcnt vmcnt(0)), so a multi-stage
+// pipeline degenerates to one stage.  Issued through asm the transfers are
+// invisible to that analysis, and a kernel using these helpers must itself
+// wait (s_waitcnt vmcnt) for the transfers that filled a buffer, then pass a
+// barrier, before any wave reads that buffer; vector-memory loads complete
+// in issue order, so vmcnt(n) leaves only the n most recent in flight.
+// The s_nop covers the wait state a transfer needs after m0 is written; m0
+// holds no compiler value across these statements in the kernels that use
+// them (they issue no other m0-using instruction).
+#pragma once
+
+#include <stdint.h>
+
+namespace dqkv {
+
+typedef __attribute__((address_space(3))) void lds_dma_t;
+
+// 64-bit per-lane source address.
+__device__ __forceinline__ void dma16(const void* g, lds_dma_t* l) {
+  const uint32_t m = (uint32_t)(size_t)l;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(m) : "memory", "m0");
+}
+
+// Wave-uniform base (moved to scalar registers) plus a 32-bit per-lane byte
+// offset, so the per-tile address arithmetic stays on the scalar unit.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, lds_dma_t* l) {
+  const uint32_t m = (uint32_t)(size_t)l;
+  const uint64_t a = (uint64_t)base;
+  const uint64_t su = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"((const void*)su), "s"(m) : "memory", "m0");
+}
+
+}  // namespace dqkv

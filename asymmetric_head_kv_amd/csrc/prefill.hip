@@ -35,6 +35,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace dqkv {
 
@@ -44,7 +45,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kPfWaves = 4;
@@ -74,33 +74,6 @@ struct PfLds {
   __device__ static int kswz(int j) { return (j / KR256) & (K16 - 1); }
   __device__ static int vswz(int j) { return 4 * ((j / VR256) & (V16 / 4 - 1)); }
 };
-
-// One 16-byte-per-lane HBM -> LDS transfer (global_load_lds_dwordx4): lane
-// i's 16 bytes from g land at LDS address l + 16 i, l in m0.  Issued through
-// asm because the compiler cannot tell the LDS stages apart: after the
-// builtin form it makes the first LDS read that follows wait (vmcnt 0) for
-// the transfer, which exposed the whole HBM latency of the next tile in every
-// step.  The key loop waits for these transfers itself (vmcnt 0, then the
-// barrier) before any wave reads the stage they fill; the s_nop covers the
-// one wait state a transfer needs after m0 is written.
-__device__ __forceinline__ void dma16(const void* g, lds_void* l) {
-  const uint32_t m = (uint32_t)(size_t)l;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(m) : "memory", "m0");
-}
-
-// The same transfer from a wave-uniform base (SGPR pair) plus a per-lane
-// byte offset, so that the per-tile address arithmetic stays on the scalar
-// unit.
-__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, lds_void* l) {
-  const uint32_t m = (uint32_t)(size_t)l;
-  const uint64_t a = (uint64_t)base;
-  const uint64_t su = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  base = (const void*)su;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(base), "s"(m) : "memory", "m0");
-}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
@@ -225,12 +198,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     if (j0 + kPfKeys <= n_keys) {
       const bf16* tb = kbase + (size_t)(j0 & row_mask) * DK;
 #pragma unroll
-      for (int r = 0; r < KR; ++r) dma16s(tb, k_vo[r], (lds_void*)(kl + r * 4096));
+      for (int r = 0; r < KR; ++r) dma16s(tb, k_vo[r], (lds_dma_t*)(kl + r * 4096));
     } else {
 #pragma unroll
       for (int r = 0; r < KR; ++r) {
         const int j = min(j0 + k_row(r), n_keys - 1);
-        dma16(kbase + (uint32_t)((j & row_mask) * DK + k_off(r)), (lds_void*)(kl + r * 4096));
+        dma16(kbase + (uint32_t)((j & row_mask) * DK + k_off(r)), (lds_dma_t*)(kl + r * 4096));
       }
     }
   };
@@ -241,12 +214,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     if (j0 + kPfKeys <= n_keys) {
       const bf16* tb = vbase + (size_t)(j0 & row_mask) * DV;
 #pragma unroll
-      for (int r = 0; r < VR; ++r) dma16s(tb, v_vo[r], (lds_void*)(vl + r * 4096));
+      for (int r = 0; r < VR; ++r) dma16s(tb, v_vo[r], (lds_dma_t*)(vl + r * 4096));
     } else {
 #pragma unroll
       for (int r = 0; r < VR; ++r) {
         const int j = min(j0 + v_row(r), n_keys - 1);
-        dma16(vbase + (uint32_t)((j & row_mask) * DV + v_off(r)), (lds_void*)(vl + r * 4096));
+        dma16(vbase + (uint32_t)((j & row_mask) * DV + v_off(r)), (lds_dma_t*)(vl + r * 4096));
       }
     }
   };
