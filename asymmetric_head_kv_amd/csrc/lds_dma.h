@@ -30,13 +30,16 @@ __device__ __forceinline__ void dma16(const void* g, lds_dma_t* l) {
 }
 
 // Wave-uniform base (moved to scalar registers) plus a 32-bit per-lane byte
-// offset, so the per-tile address arithmetic stays on the scalar unit.
+// offset, so the per-tile address arithmetic stays on the scalar unit.  A
+// vector-memory instruction that reads an SGPR written by a VALU instruction
+// (here v_readfirstlane) needs 5 wait states in between, which the compiler
+// cannot see through the asm: the leading s_nop 4 provides them.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, lds_dma_t* l) {
   const uint32_t m = (uint32_t)(size_t)l;
   const uint64_t a = (uint64_t)base;
   const uint64_t su = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"((const void*)su), "s"(m) : "memory", "m0");
 }
 
