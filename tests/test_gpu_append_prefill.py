@@ -159,3 +159,29 @@ def test_prefill_last_row_matches_decode():
     torch.cuda.synchronize()
     dec = to_host(out)
     assert_close(got[:, -1], dec, "bf16", "last row")
+
+
+TINY = [
+    # t_new, lengths (after append), l_cap: one new row of a 100-row sequence
+    # (two key tiles over four key splits, so two splits see no key), one
+    # row on a one-row cache, and a batch whose second sequence is shorter
+    # than a tile.
+    (1, [100], 128),
+    (1, [1], 64),
+    (3, [3000, 65], 3008),
+]
+
+
+@pytest.mark.parametrize("cfg", TINY, ids=lambda c: f"t{c[0]}-L{'-'.join(map(str, c[1]))}")
+def test_prefill_tiny_and_empty_key_splits(cfg):
+    T, lens, cap = cfg
+    case = synth.make_case(205, dtype="bf16", batch=len(lens), n_q=16, n_k=4, n_v=16, d_k=64,
+                           d_v=128, ctx_len=lens, l_cap=cap, t_new=T, poison_tail=True)
+    q, k, v = case.widened()
+    ref, ref_lse = oracle.prefill(q, k, v, case.ctx_len, case.scale)
+    for with_lse, split in ((True, True), (False, True), (True, False)):
+        _say("prefill tiny", cfg, "lse" if with_lse else "no lse", "split" if split else "unsplit")
+        got, lse = run_prefill(case, with_lse, split)
+        assert_close(got, ref, "bf16", f"{cfg} lse={with_lse} split={split}")
+        if with_lse:
+            assert_lse_close(lse, ref_lse, "bf16", str(cfg))
