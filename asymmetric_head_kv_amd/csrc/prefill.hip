@@ -11,7 +11,8 @@
 // tiles of 64 through two LDS stages, software-pipelined so that the matrix
 // products of one tile overlap the softmax of another inside each wave (see
 // the key loop).  Tiles travel from HBM straight into LDS (16-byte
-// global_load_lds, no register staging): K and V row-major, their 16-byte
+// global_load_lds through lds_dma.h, no register staging; the key loop's
+// own vmcnt waits and barriers order them): K and V row-major, their 16-byte
 // slots XOR-swizzled by row against bank conflicts.  The V^T operand
 // is read with ds_read_b64_tr_b16, which hands each lane one value column for
 // four consecutive keys, so V needs no rearranging.  Everything is computed
