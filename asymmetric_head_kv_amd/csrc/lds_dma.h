@@ -11,6 +11,7 @@
 // wait (s_waitcnt vmcnt) for the transfers that filled a buffer, then pass a
 // barrier, before any wave reads that buffer; vector-memory loads complete
 // in issue order, so vmcnt(n) leaves only the n most recent in flight.
+// The LDS address must be wave-uniform (it is taken from the first lane).
 // The s_nop covers the wait state a transfer needs after m0 is written; m0
 // holds no compiler value across these statements in the kernels that use
 // them (they issue no other m0-using instruction).
@@ -24,7 +25,7 @@ typedef __attribute__((address_space(3))) void lds_dma_t;
 
 // 64-bit per-lane source address.
 __device__ __forceinline__ void dma16(const void* g, lds_dma_t* l) {
-  const uint32_t m = (uint32_t)(size_t)l;
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)l);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(g), "s"(m) : "memory", "m0");
 }
@@ -35,7 +36,7 @@ __device__ __forceinline__ void dma16(const void* g, lds_dma_t* l) {
 // (here v_readfirstlane) needs 5 wait states in between, which the compiler
 // cannot see through the asm: the leading s_nop 4 provides them.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, lds_dma_t* l) {
-  const uint32_t m = (uint32_t)(size_t)l;
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)l);
   const uint64_t a = (uint64_t)base;
   const uint64_t su = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
