@@ -23,6 +23,12 @@ namespace dqkv {
 
 typedef __attribute__((address_space(3))) void lds_dma_t;
 
+// m0 is listed as clobbered for the reader; the compiler warns that it does
+// not preserve reserved registers around asm, which is moot here (see above:
+// no compiler value lives in m0 in these kernels).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
 // 64-bit per-lane source address.
 __device__ __forceinline__ void dma16(const void* g, lds_dma_t* l) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)l);
@@ -43,5 +49,7 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, lds_dma_
   asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"((const void*)su), "s"(m) : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 }  // namespace dqkv
