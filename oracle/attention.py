@@ -16,7 +16,7 @@ storage type.  The softmax is two-pass (maximum, then normalised exponentials)
 and unchunked: it deliberately shares no structure with the split/online GPU
 kernels.  numpy's matrix-vector product is the only library step.
 
-Readings taken where the pages are silent (all listed in the design doc):
+Readings taken where the pages are silent:
 * scale defaults to 1/sqrt(d_k)                (architecture page, §3.4 Step 4)
 * head maps are floor(i * n_h / n_q), 0-based  (§3.4 Step 3; FlexHeadFA section)
 * the newest token attends to itself: ctx_len counts the rows after the

@@ -14,7 +14,7 @@ query.  With weights in the usual (out, in) layout:
     a = silu(g) * u,  silu(x) = x / (1 + e^{-x})
     q = a W_down^T                          (M x n_q d_k)
 
-Readings (listed in the design doc): SwiGLU is the usual silu-gated product
+Readings taken here: SwiGLU is the usual silu-gated product
 (Shazeer's GLU variant, which the page names); 3072 is the width of the gated
 intermediate layer (d_h^q), and the query that enters attention has n_q heads
 of d_k dimensions (section 3.4 Step 3 defines q_(t,i) in R^{d_h^k}); there are
