@@ -12,7 +12,14 @@
 namespace {
 
 constexpr int kCUs = 256;             // MI355X compute units
-constexpr int kWavesPerCUTarget = 8;  // split waves to aim for per CU
+// Split waves to aim for per CU.  Contiguous caches: one four-wave
+// workgroup per CU in one round (32k x 1 sequence: 512-row chunks, 29.5 us
+// per step against 30.5 at 256-row chunks with two per CU; a fraction of a
+// second round, e.g. 448-row chunks, costs 25%).  Paged caches keep two per
+// CU: each 64-row tile sits in its own page, and the second wave per SIMD
+// hides that latency (512-row chunks: 33.2 us against 30.8).
+constexpr int kWavesPerCUContig = 4;
+constexpr int kWavesPerCUPaged = 8;
 constexpr int kMaxChunks = 8192;      // bounds the workspace and the combine's loop
 // Batches of at least kRaggedBatch sequences plan kRaggedOversub times more
 // split workgroups: the host cannot see the lengths (they stay on the
@@ -47,10 +54,11 @@ int to_status(hipError_t e) { return e == hipSuccess ? DQKV_OK : DQKV_ERR_HIP; }
 // Rows per context chunk: enough (sequence, head-quad, chunk) workgroups to
 // give every CU about kWavesPerCUTarget waves (times kRaggedOversub for
 // large batches), in multiples of 64 rows.  H = query heads per wave.
-int plan_chunk_h(int n_q, int H, int batch, int max_ctx) {
+int plan_chunk_h(int n_q, int H, int batch, int max_ctx, bool paged) {
   long long quads = (long long)batch * ((n_q / H + 3) / 4);
   if (quads < 1) quads = 1;  // an empty batch launches nothing
-  const long long want_wg = (long long)kCUs * kWavesPerCUTarget / 4 *
+  const int waves = (paged || batch >= kRaggedBatch) ? kWavesPerCUPaged : kWavesPerCUContig;
+  const long long want_wg = (long long)kCUs * waves / 4 *
                             (batch >= kRaggedBatch ? kRaggedOversub : 1);
   long long chunks_per_seq = (want_wg + quads - 1) / quads;
   if (chunks_per_seq < 1) chunks_per_seq = 1;
@@ -63,11 +71,11 @@ int plan_chunk_h(int n_q, int H, int batch, int max_ctx) {
   return (int)S;
 }
 
-int plan_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx) {
+int plan_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx, bool paged) {
   // Waves per (sequence, chunk): one per query head, or per pair of query
   // heads that share their K and V heads (see the split kernel).
   const int H = (n_q == 2 * n_v && (n_q / n_k) % 2 == 0) ? 2 : 1;
-  return plan_chunk_h(n_q, H, batch, max_ctx);
+  return plan_chunk_h(n_q, H, batch, max_ctx, paged);
 }
 
 int chunks_for(int max_ctx, int S) {
@@ -102,9 +110,9 @@ size_t workspace_bytes(int n_q, int d_v, int batch, int C) {
 }
 
 int resolve_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx, int chunk_tokens,
-                  int* S) {
+                  int* S, bool paged = false) {
   if (chunk_tokens < 0 || chunk_tokens % kMinChunk != 0) return DQKV_ERR_SHAPE;
-  *S = chunk_tokens ? chunk_tokens : plan_chunk(n_q, n_k, n_v, batch, max_ctx);
+  *S = chunk_tokens ? chunk_tokens : plan_chunk(n_q, n_k, n_v, batch, max_ctx, paged);
   if (chunks_for(max_ctx, *S) > kMaxChunks) return DQKV_ERR_UNSUPPORTED;
   return DQKV_OK;
 }
@@ -179,10 +187,14 @@ int32_t diffqkv_decode_workspace(int32_t n_q, int32_t n_k, int32_t n_v, int32_t 
   int st = check_heads(n_q, n_k, n_v, d_k, d_v);
   if (st) return st;
   if (batch < 0 || max_ctx < 0) return DQKV_ERR_SHAPE;
-  int S = 0;
+  // With the automatic choice: enough for the contiguous and the paged plan
+  // (the paged one never has fewer chunks).
+  int S = 0, Sp = 0;
   st = resolve_chunk(n_q, n_k, n_v, batch, max_ctx, chunk_tokens, &S);
   if (st) return st;
-  *bytes = workspace_bytes(n_q, d_v, batch, chunks_for(max_ctx, S));
+  st = resolve_chunk(n_q, n_k, n_v, batch, max_ctx, chunk_tokens, &Sp, true);
+  if (st) return st;
+  *bytes = workspace_bytes(n_q, d_v, batch, chunks_for(max_ctx, S < Sp ? S : Sp));
   return DQKV_OK;
 }
 
@@ -217,7 +229,7 @@ static int prepare_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, in
                           const void* v_cache, const int32_t* ctx_len, void* out,
                           float* lse, int32_t chunk_tokens, void* workspace,
                           size_t workspace_bytes_given, void* stream, bool need_qkv,
-                          bool need_out, dqkv::DecodeArgs* a) {
+                          bool need_out, dqkv::DecodeArgs* a, bool paged = false) {
   int st = check_heads(n_q, n_k, n_v, d_k, d_v);
   if (st) return st;
   st = check_dtype_dims(dtype, d_k, d_v);
@@ -232,7 +244,7 @@ static int prepare_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, in
       (need_out && !aligned16(out)) || !aligned16(workspace))
     return DQKV_ERR_ALIGN;
   int S = 0;
-  st = resolve_chunk(n_q, n_k, n_v, batch, max_ctx, chunk_tokens, &S);
+  st = resolve_chunk(n_q, n_k, n_v, batch, max_ctx, chunk_tokens, &S, paged);
   if (st) return st;
   const int C = chunks_for(max_ctx, S);
   if ((long long)(n_q + 3) / 4 > 65535) return DQKV_ERR_UNSUPPORTED;
@@ -576,7 +588,7 @@ int32_t diffqkv_decode_paged(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
   dqkv::DecodeArgs a;
   st = prepare_decode(n_q, n_k, n_v, d_k, d_v, dtype, batch, cap, max_ctx, scale, q, k_pages,
                       v_pages, ctx_len, out, lse, chunk_tokens, workspace,
-                      workspace_bytes_given, stream, true, true, &a);
+                      workspace_bytes_given, stream, true, true, &a, true);
   if (st) return st;
   if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return DQKV_ERR_ALIGN;
   a.k_new = k_new;

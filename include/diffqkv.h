@@ -76,7 +76,8 @@ const char* dqkv_status_str(int32_t status);
 
 /*
  * Context-chunk length (rows per split) that diffqkv_decode uses when it is
- * called with chunk_tokens = 0.  Pure host computation.
+ * called with chunk_tokens = 0.  (diffqkv_decode_paged plans its own: half
+ * as long for batches under 8 sequences.)  Pure host computation.
  */
 int32_t diffqkv_decode_chunk(int32_t n_q, int32_t n_k, int32_t n_v,
                              int32_t d_k, int32_t d_v, int32_t batch,
@@ -84,7 +85,8 @@ int32_t diffqkv_decode_chunk(int32_t n_q, int32_t n_k, int32_t n_v,
 
 /*
  * Workspace bytes diffqkv_decode needs for these sizes and chunk length
- * (chunk_tokens = 0: the automatic choice).  The workspace holds the
+ * (chunk_tokens = 0: the automatic choices of both diffqkv_decode and
+ * diffqkv_decode_paged, whichever needs more).  The workspace holds the
  * per-chunk partial results (running max, sum and weighted V sum, fp32) of
  * the split step.  Pure host computation.
  */

@@ -97,22 +97,24 @@ def test_decode_null_alignment_and_workspace(lib):
 
 def test_workspace_and_chunk_plan(lib):
     # Partials: (m, l) then acc[d_v], fp32, per (sequence, query head, chunk).
-    for (B, n_q, d_v, ctx) in [(1, 16, 128, 32768), (16, 16, 128, 32769), (4, 16, 128, 65536),
-                               (1, 4, 64, 256)]:
+    # The automatic chunk of diffqkv_decode (contiguous caches) and that of
+    # diffqkv_decode_paged (half as long for batches under 8 sequences); the
+    # workspace query covers both.
+    for (B, n_q, d_v, ctx, S_contig, S_paged) in [(1, 16, 128, 32768, 512, 256),
+                                                  (16, 16, 128, 32769, 576, 576),
+                                                  (4, 16, 128, 65536, 4096, 2048),
+                                                  (1, 4, 64, 256, 64, 64)]:
         S = dq.decode_chunk(n_q, 4 if n_q > 4 else 1, n_q, 64, d_v, B, ctx)
-        assert S % 64 == 0 and S >= 64
-        C = -(-ctx // S)
+        assert S == S_contig
+        C = max(-(-ctx // S), -(-ctx // S_paged))
         parts = B * n_q * C
         expect = -(-parts * 8 // 256) * 256 + parts * d_v * 4
         assert dq.decode_workspace_bytes(n_q, 4 if n_q > 4 else 1, n_q, 64, d_v, B, ctx) == expect
-    # Long single sequence: enough chunks to spread over the chip.
-    S = dq.decode_chunk(16, 4, 16, 64, 128, 1, 32768)
-    assert 32768 // S >= 64
-    # Large batches (lengths unknown to the host, possibly ragged) plan about
-    # eight times more chunks than a small batch of the same capacity would.
-    S4 = dq.decode_chunk(16, 4, 16, 64, 128, 4, 65536)
-    S16 = dq.decode_chunk(16, 4, 16, 64, 128, 16, 32769)
-    assert 65536 // S4 == 32 and -(-32769 // S16) >= 32
+    # Long single sequence: one four-wave workgroup per CU (4 K groups x 64
+    # chunks).  Large batches (lengths unknown to the host, possibly ragged)
+    # plan about eight times more chunks than a small batch would.
+    assert 32768 // dq.decode_chunk(16, 4, 16, 64, 128, 1, 32768) == 64
+    assert -(-32769 // dq.decode_chunk(16, 4, 16, 64, 128, 16, 32769)) >= 32
     # Explicit chunk lengths are honoured.
     assert dq.decode_workspace_bytes(16, 4, 16, 64, 128, 1, 4096, 64) == \
         -(-16 * 64 * 8 // 256) * 256 + 16 * 64 * 128 * 4

@@ -115,7 +115,9 @@ def test_paged_decode_matches_contiguous_and_oracle(cfg):
     case = synth.make_case(402, dtype=dtype, batch=len(lens), n_q=n_q, n_k=n_k, n_v=n_v,
                            d_k=d_k, d_v=d_v, ctx_len=lens, l_cap=cap)
     _say("paged decode", cfg)
-    for chunk in (0, 192):
+    # Same chunking: bit-identical (the contiguous default, and 192 rows).
+    S0 = dq.decode_chunk(n_q, n_k, n_v, d_k, d_v, len(lens), cap)
+    for chunk in (S0, 192):
         out_p, lse_p, _ = run_paged(case, P, seed=P + chunk, chunk=chunk)
         q, k, v, ctx = upload(case)
         lse_c = torch.empty_like(lse_p)
@@ -123,6 +125,8 @@ def test_paged_decode_matches_contiguous_and_oracle(cfg):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(raw_host(out_p), raw_host(out_c))
         np.testing.assert_array_equal(lse_p.cpu().numpy(), lse_c.cpu().numpy())
+    # The paged path's own default chunking, against the oracle.
+    out_p, lse_p, _ = run_paged(case, P, seed=P)
     qw, kw, vw = case.widened()
     ref, ref_lse = oracle.decode(qw, kw, vw, case.ctx_len, case.scale)
     err = assert_close(to_host(out_p), ref, dtype, f"paged {cfg}")
@@ -191,12 +195,16 @@ def test_kv_append_paged_against_oracle(dtype):
 def test_paged_full_workload(P):
     case = synth.make_case(**synth.workload("decode32k_asym"))
     _say("paged full workload decode32k_asym, page rows", P)
-    out_p, lse_p, _ = run_paged(case, P, seed=P)
+    # With the contiguous default chunking: bit-identical to the contiguous
+    # decode; with its own default: within tolerance of the oracle.
+    S0 = dq.decode_chunk(case.n_q, case.n_k, case.n_v, case.d_k, case.d_v, case.batch, case.l_cap)
+    out_p, lse_p, _ = run_paged(case, P, seed=P, chunk=S0)
     q, k, v, ctx = upload(case)
     lse_c = torch.empty_like(lse_p)
     out_c, _ = dq.decode(q, k, v, ctx, scale=case.scale, lse=lse_c)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(raw_host(out_p), raw_host(out_c))
+    out_p, lse_p, _ = run_paged(case, P, seed=P)
     qw, kw, vw = case.widened()
     ref, ref_lse = oracle.decode(qw, kw, vw, case.ctx_len, case.scale)
     err = assert_close(to_host(out_p), ref, "bf16", "paged 32k")
@@ -347,7 +355,9 @@ def test_paged_decode_full_size_matches_contiguous():
     vp[perm] = v[0].view(16, n_pg, P, 128).permute(1, 0, 2, 3)
     table = perm.to(torch.int32).view(1, n_pg)
     _say("paged decode, full size", L, "pages", n_pg)
-    out_p, _ = dq.decode_paged(q, kp, vp, table, ctx, max_ctx=L, scale=case.scale)
+    S0 = dq.decode_chunk(16, 4, 16, 64, 128, 1, L)  # the same chunking for both
+    out_p, _ = dq.decode_paged(q, kp, vp, table, ctx, max_ctx=L, scale=case.scale,
+                               chunk_tokens=S0)
     out_c, _ = dq.decode(q, k, v, ctx, scale=case.scale)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(raw_host(out_p), raw_host(out_c))
