@@ -120,7 +120,7 @@ int resolve_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx, int chunk_t
 // Workspace of a selective-V decode: logits, per-range (max, sum), and the
 // per-range candidates (logit, row).
 struct SelLayout {
-  int S, C, ld_s, n_ranges;
+  int S, C, ld_s, range_rows, n_ranges;
   size_t off_ml, off_cs, off_ci, total;
 };
 
@@ -142,7 +142,15 @@ int selective_layout(int n_q, int n_k, int batch, int max_ctx, int top_k, SelLay
   if (o->C > kMaxChunks) return DQKV_ERR_UNSUPPORTED;
   o->ld_s = (int)(((long long)max_ctx + 63) / 64 * 64);
   if (o->ld_s < 64) o->ld_s = 64;
-  o->n_ranges = (int)(((long long)max_ctx + dqkv::kSelRows - 1) / dqkv::kSelRows);
+  // Shorter ranges when the longer ones would leave CUs without a local
+  // selection (32k x 1 sequence x 16 heads: 8 ranges each -> 128 workgroups;
+  // 2048-row ranges: 26.9 -> 23.0 us per step; with enough workgroups the
+  // longer ranges win, as the final selection then merges half the
+  // candidates: 4 x 64k, 53.9 against 67.0 us).
+  const long long long_ranges = ((long long)max_ctx + dqkv::kSelRows - 1) / dqkv::kSelRows;
+  o->range_rows = (long long)batch * n_q * long_ranges < kCUs ? dqkv::kSelRowsShort
+                                                               : dqkv::kSelRows;
+  o->n_ranges = (int)(((long long)max_ctx + o->range_rows - 1) / o->range_rows);
   if (o->n_ranges < 1) o->n_ranges = 1;
   const size_t heads = (size_t)batch * n_q;
   o->off_ml = align256(heads * o->ld_s * sizeof(float));
@@ -475,6 +483,7 @@ static int run_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int
   a.n_q = n_q; a.n_k = n_k; a.n_v = n_v; a.d_k = d_k; a.d_v = d_v;
   a.batch = batch; a.l_cap = l_cap; a.max_ctx = max_ctx;
   a.S = lay.S; a.C = lay.C; a.ld_s = lay.ld_s; a.n_ranges = lay.n_ranges;
+  a.range_rows = lay.range_rows;
   a.top_k = top_k; a.scale = scale;
   a.q = q; a.k_cache = k_cache; a.v_cache = v_cache; a.ctx_len = ctx_len;
   a.out = out; a.lse = lse; a.sel_idx = sel_idx;

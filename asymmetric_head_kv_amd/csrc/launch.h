@@ -80,8 +80,11 @@ struct PrefillArgs {
   hipStream_t stream;
 };
 
-// Selective-V decode: rows per local-selection range, and the largest top_k.
+// Selective-V decode: rows per local-selection range (planned: the longer
+// one unless that leaves fewer workgroups than compute units), and the
+// largest top_k.
 constexpr int kSelRows = 4096;
+constexpr int kSelRowsShort = 2048;
 constexpr int kMaxTopK = 1024;
 
 struct SelectiveArgs {
@@ -90,7 +93,8 @@ struct SelectiveArgs {
   int batch, l_cap, max_ctx;
   int S, C;       // score-kernel chunk rows, chunks per sequence
   int ld_s;       // row stride of the logit buffer (max_ctx rounded up to 64)
-  int n_ranges;   // ceil(max_ctx / kSelRows)
+  int range_rows; // rows per local-selection range: kSelRows or kSelRowsShort
+  int n_ranges;   // ceil(max_ctx / range_rows)
   int top_k;
   float scale;
   const void* q;

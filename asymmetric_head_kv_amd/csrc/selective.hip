@@ -12,7 +12,7 @@
 //              64-row tile of a K head and all the query heads that share it
 //              (up to 16), so every K row is read once; bf16 products run on
 //              the matrix cores, fp32 ones on the vector ALUs.
-//   2. local:  per (query head, range of kSelRows rows): the range's max and
+//   2. local:  per (query head, range of 2048 or 4096 rows): the range's max and
 //              sum of 2^(s - max), and its own top_k rows (a row in the
 //              global top_k is in its range's top_k), kept in index order.
 //   3. gather: per query head: merge the ranges' (max, sum) into the full
@@ -287,7 +287,7 @@ __device__ __forceinline__ void reg_compact(const uint32_t (&key)[E], int n, Thr
   }
 }
 
-constexpr int kSelE = kSelRows / kSelThreads;  // keys per thread
+constexpr int kSelE = kSelRows / kSelThreads;  // keys per thread of the longest range
 
 // ------------------------------------------------------------ 1. scores
 
@@ -446,13 +446,15 @@ __global__ __launch_bounds__(256) void sel_score_mfma_kernel(
 
 // ------------------------------------------------- 2. per-range selection
 
-// One workgroup per (query head, range of kSelRows rows); candidates of
-// range rg are written at [rg * top_k, rg * top_k + min(top_k, rows)), so a
-// head's candidate list is contiguous and in ascending row order.
+// One workgroup per (query head, range of RS rows); candidates of range rg
+// are written at [rg * top_k, rg * top_k + min(top_k, rows)), so a head's
+// candidate list is contiguous and in ascending row order.
+template <int RS>
 __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_len,
     float* __restrict__ range_ml, float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
     int n_q, int l_cap, int max_ctx, int ld_s, int n_ranges, int top_k) {
+  constexpr int E = RS / kSelThreads;  // keys per thread
   __shared__ __align__(16) uint32_t hist[3 * kBins];
   __shared__ int red[8];
   __shared__ float wm[4], wl[4];
@@ -460,26 +462,26 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int L = ctx_len[b];
   L = max(0, min(L, min(max_ctx, l_cap)));
-  const int j0 = rg * kSelRows;
+  const int j0 = rg * RS;
   if (j0 >= L) return;
-  const int rows = min(kSelRows, L - j0);
+  const int rows = min(RS, L - j0);
   const float* sc = scores + ((size_t)b * n_q + i) * ld_s + j0;
 
-  float s[kSelE];
+  float s[E];
 #pragma unroll
-  for (int e = 0; e < kSelE; ++e) {
-    const int x = reg_index<kSelE>(e);
+  for (int e = 0; e < E; ++e) {
+    const int x = reg_index<E>(e);
     s[e] = x < rows ? sc[x] : -INFINITY;
   }
   clear_hists(hist);
   // The range's max and sum of 2^(s - max): per wave, then over the waves.
   float m = s[0];
 #pragma unroll
-  for (int e = 1; e < kSelE; ++e) m = fmaxf(m, s[e]);
+  for (int e = 1; e < E; ++e) m = fmaxf(m, s[e]);
   m = wave_max(m);
   float l = 0.f;
 #pragma unroll
-  for (int e = 0; e < kSelE; ++e) l += reg_index<kSelE>(e) < rows ? fast_exp2(s[e] - m) : 0.f;
+  for (int e = 0; e < E; ++e) l += reg_index<E>(e) < rows ? fast_exp2(s[e] - m) : 0.f;
   l = wave_sum(l);
   if (lane == 0) {
     wm[wave] = m;
@@ -499,8 +501,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
   int32_t* ci = cand_i + slot * top_k;
   if (rows <= top_k) {  // the whole range is a candidate
 #pragma unroll
-    for (int e = 0; e < kSelE; ++e) {
-      const int x = reg_index<kSelE>(e);
+    for (int e = 0; e < E; ++e) {
+      const int x = reg_index<E>(e);
       if (x < rows) {
         cs[x] = s[e];
         ci[x] = j0 + x;
@@ -508,26 +510,28 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
     }
     return;
   }
-  uint32_t key[kSelE];
+  uint32_t key[E];
 #pragma unroll
-  for (int e = 0; e < kSelE; ++e) key[e] = order_key(s[e]);
-  const Threshold th = reg_select_threshold<kSelE>(key, rows, top_k, hist, red);
-  reg_compact<kSelE>(key, rows, th, red, [&](int pos, int e) {
+  for (int e = 0; e < E; ++e) key[e] = order_key(s[e]);
+  const Threshold th = reg_select_threshold<E>(key, rows, top_k, hist, red);
+  reg_compact<E>(key, rows, th, red, [&](int pos, int e) {
     if (pos < top_k) {
       cs[pos] = s[e];
-      ci[pos] = j0 + reg_index<kSelE>(e);
+      ci[pos] = j0 + reg_index<E>(e);
     }
   });
 }
 
 // ------------------------------------------ 3. final selection and gather
 
-template <typename T, int DV>
+// E: candidate keys per thread held in registers (E * kSelThreads of them).
+template <typename T, int DV, int E>
 __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
     const T* vc, const int32_t* __restrict__ ctx_len, const float* __restrict__ range_ml,
     const float* __restrict__ cand_s, const int32_t* __restrict__ cand_i, T* __restrict__ out,
     float* __restrict__ lse, int32_t* __restrict__ sel_idx, int n_q, int n_v, int l_cap,
-    int max_ctx, int n_ranges, int top_k, const T* __restrict__ v_new, T* vc_w, PageMap pm) {
+    int max_ctx, int n_ranges, int range_rows, int top_k, const T* __restrict__ v_new, T* vc_w,
+    PageMap pm) {
   constexpr int EPL = Elem<T>::kPer16;
   constexpr int LPR = DV / EPL;               // lanes per V row
   constexpr int RPP = kSelThreads / LPR;      // V rows per pass of the block
@@ -553,18 +557,18 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
   // Candidates: range r contributed min(top_k, rows of r) entries at
   // [r * top_k, ...); all ranges but the last are full, so the n_c entries
   // are contiguous and in ascending row order.
-  const int nr = (L + kSelRows - 1) / kSelRows;
-  const int n_c = nr == 0 ? 0 : (nr - 1) * top_k + min(top_k, L - (nr - 1) * kSelRows);
+  const int nr = (L + range_rows - 1) / range_rows;
+  const int n_c = nr == 0 ? 0 : (nr - 1) * top_k + min(top_k, L - (nr - 1) * range_rows);
   const int kk = min(top_k, L);
   const float* cs = cand_s + head * n_ranges * top_k;
   const int32_t* ci = cand_i + head * n_ranges * top_k;
-  const bool in_regs = n_c <= kSelRows;
-  float s[kSelE];
-  int32_t idx[kSelE];
+  const bool in_regs = n_c <= E * kSelThreads;
+  float s[E];
+  int32_t idx[E];
   if (in_regs) {
 #pragma unroll
-    for (int e = 0; e < kSelE; ++e) {
-      const int p = reg_index<kSelE>(e);
+    for (int e = 0; e < E; ++e) {
+      const int p = reg_index<E>(e);
       s[e] = p < n_c ? cs[p] : -INFINITY;
       idx[e] = p < n_c ? ci[p] : 0;
     }
@@ -593,14 +597,14 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
     };
     if (n_c <= kk) {
 #pragma unroll
-      for (int e = 0; e < kSelE; ++e)
-        if (reg_index<kSelE>(e) < n_c) take(reg_index<kSelE>(e), e);
+      for (int e = 0; e < E; ++e)
+        if (reg_index<E>(e) < n_c) take(reg_index<E>(e), e);
     } else {
-      uint32_t key[kSelE];
+      uint32_t key[E];
 #pragma unroll
-      for (int e = 0; e < kSelE; ++e) key[e] = order_key(s[e]);
-      const Threshold th = reg_select_threshold<kSelE>(key, n_c, kk, hist, red);
-      reg_compact<kSelE>(key, n_c, th, red, take);
+      for (int e = 0; e < E; ++e) key[e] = order_key(s[e]);
+      const Threshold th = reg_select_threshold<E>(key, n_c, kk, hist, red);
+      reg_compact<E>(key, n_c, th, red, take);
     }
   } else {  // more candidates than registers hold: passes over global memory
     auto take = [&](int pos, int p) {
@@ -699,10 +703,19 @@ static hipError_t launch_score_t(const SelectiveArgs& a) {
 
 template <typename T, int DV>
 static hipError_t launch_gather_t(const SelectiveArgs& a) {
-  hipLaunchKernelGGL((sel_gather_kernel<T, DV>), dim3(a.n_q, a.batch), dim3(kSelThreads), 0,
-                     a.stream, (const T*)a.v_cache, a.ctx_len, a.range_ml, a.cand_s, a.cand_i,
-                     (T*)a.out, a.lse, a.sel_idx, a.n_q, a.n_v, a.l_cap, a.max_ctx,
-                     a.n_ranges, a.top_k, (const T*)a.v_new, (T*)a.v_cache, a.pages);
+  // Half the registers when every candidate fits in 8 per thread.
+  if ((long long)a.n_ranges * a.top_k <= 8 * kSelThreads)
+    hipLaunchKernelGGL((sel_gather_kernel<T, DV, 8>), dim3(a.n_q, a.batch), dim3(kSelThreads),
+                       0, a.stream, (const T*)a.v_cache, a.ctx_len, a.range_ml, a.cand_s,
+                       a.cand_i, (T*)a.out, a.lse, a.sel_idx, a.n_q, a.n_v, a.l_cap, a.max_ctx,
+                       a.n_ranges, a.range_rows, a.top_k, (const T*)a.v_new, (T*)a.v_cache,
+                       a.pages);
+  else
+    hipLaunchKernelGGL((sel_gather_kernel<T, DV, kSelE>), dim3(a.n_q, a.batch),
+                       dim3(kSelThreads), 0, a.stream, (const T*)a.v_cache, a.ctx_len,
+                       a.range_ml, a.cand_s, a.cand_i, (T*)a.out, a.lse, a.sel_idx, a.n_q,
+                       a.n_v, a.l_cap, a.max_ctx, a.n_ranges, a.range_rows, a.top_k,
+                       (const T*)a.v_new, (T*)a.v_cache, a.pages);
   return hipGetLastError();
 }
 
@@ -751,9 +764,16 @@ static hipError_t gather_dv(const SelectiveArgs& a) {
 hipError_t launch_decode_selective(const SelectiveArgs& a) {
   hipError_t e = a.bf16 ? score_dk<bf16>(a) : score_dk<float>(a);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sel_local_kernel, dim3(a.n_ranges, a.n_q, a.batch), dim3(kSelThreads), 0,
-                     a.stream, a.scores, a.ctx_len, a.range_ml, a.cand_s, a.cand_i, a.n_q,
-                     a.l_cap, a.max_ctx, a.ld_s, a.n_ranges, a.top_k);
+  if (a.range_rows == kSelRowsShort)
+    hipLaunchKernelGGL(sel_local_kernel<kSelRowsShort>, dim3(a.n_ranges, a.n_q, a.batch),
+                       dim3(kSelThreads), 0, a.stream, a.scores, a.ctx_len, a.range_ml,
+                       a.cand_s, a.cand_i, a.n_q, a.l_cap, a.max_ctx, a.ld_s, a.n_ranges,
+                       a.top_k);
+  else
+    hipLaunchKernelGGL(sel_local_kernel<kSelRows>, dim3(a.n_ranges, a.n_q, a.batch),
+                       dim3(kSelThreads), 0, a.stream, a.scores, a.ctx_len, a.range_ml,
+                       a.cand_s, a.cand_i, a.n_q, a.l_cap, a.max_ctx, a.ld_s, a.n_ranges,
+                       a.top_k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return a.bf16 ? gather_dv<bf16>(a) : gather_dv<float>(a);

@@ -262,8 +262,9 @@ int32_t diffqkv_prefill_paged(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k
  *             order, -1 past min(top_k, ctx_len[b]).
  *   workspace diffqkv_decode_selective_workspace bytes, 16-byte aligned,
  *             contents need not be initialised; it holds the fp32 logits
- *             ([B][n_q][max_ctx rounded up to 64]) and per-4096-row-range
- *             candidates.
+ *             ([B][n_q][max_ctx rounded up to 64]) and per-range candidates
+ *             (ranges of 4096 rows, or of 2048 when 4096-row ranges would
+ *             give fewer than 256 (sequence, head, range) selections).
  * ctx_len is clamped to [0, max_ctx]; ctx_len[b] = 0 gives out = 0,
  * lse = -inf, sel_idx = -1.  Three kernels on `stream`: logits (reads K
  * once), per-range top-k, final top-k with the V gather.

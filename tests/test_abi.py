@@ -175,8 +175,11 @@ def test_binding_refuses_cpu_tensors(lib):
 
 def test_selective_workspace_and_validation(lib):
     def layout(B, n_q, ctx, k):
+        # Local-selection ranges of 4096 rows, or 2048 when 4096-row ranges
+        # would give fewer (sequence, head, range) workgroups than 256 CUs.
         ld = max(64, -(-ctx // 64) * 64)
-        nr = max(1, -(-ctx // 4096))
+        rows = 2048 if B * n_q * max(1, -(-ctx // 4096)) < 256 else 4096
+        nr = max(1, -(-ctx // rows))
         a = lambda x: -(-x // 256) * 256
         return a(B * n_q * ld * 4) + a(B * n_q * nr * 8) + a(B * n_q * nr * k * 4) + B * n_q * nr * k * 4
 
