@@ -461,18 +461,28 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
   const int rg = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int L = ctx_len[b];
-  L = max(0, min(L, min(max_ctx, l_cap)));
+  // The range's logits are requested together with the sequence length
+  // (every one of the ld_s columns of the head's logit row exists; those at
+  // or past the length are masked once it arrives), so the two loads cost
+  // one memory round trip.
   const int j0 = rg * RS;
-  if (j0 >= L) return;
-  const int rows = min(RS, L - j0);
+  const int avail = min(RS, ld_s - j0);
   const float* sc = scores + ((size_t)b * n_q + i) * ld_s + j0;
-
   float s[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int x = reg_index<E>(e);
-    s[e] = x < rows ? sc[x] : -INFINITY;
+    s[e] = x < avail ? sc[x] : -INFINITY;
   }
+  L = max(0, min(L, min(max_ctx, l_cap)));
+  if (j0 >= L) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no wave ends with loads in flight
+    return;
+  }
+  const int rows = min(RS, L - j0);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (reg_index<E>(e) >= rows) s[e] = -INFINITY;
   clear_hists(hist);
   // The range's max and sum of 2^(s - max): per wave, then over the waves.
   float m = s[0];
@@ -543,11 +553,29 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
   __shared__ float part[RPP][DV + 4];
 
   const int i = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   int L = ctx_len[b];
+  const size_t head = (size_t)b * n_q + i;
+  // The candidate slots and the ranges' (max, sum) are requested together
+  // with the sequence length (all n_ranges slots of the head exist in the
+  // workspace; those past the length's ranges are masked once it arrives),
+  // so these loads cost one memory round trip.
+  const float* cs = cand_s + head * n_ranges * top_k;
+  const int32_t* ci = cand_i + head * n_ranges * top_k;
+  const float* ml = range_ml + head * n_ranges * 2;
+  const int n_slots = n_ranges * top_k;
+  float s[E];
+  int32_t idx[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int p = reg_index<E>(e);
+    s[e] = p < n_slots ? cs[p] : -INFINITY;
+    idx[e] = p < n_slots ? ci[p] : 0;
+  }
+  const float ml_m = lane < n_ranges ? ml[2 * lane] : -INFINITY;
+  const float ml_l = lane < n_ranges ? ml[2 * lane + 1] : 0.f;
   L = max(0, min(L, min(max_ctx, l_cap)));
   const int hv = (i * n_v) / n_q;
-  const size_t head = (size_t)b * n_q + i;
   const bool fused = v_new != nullptr;
   const T* vn = fused ? v_new + ((size_t)b * n_v + hv) * DV : nullptr;
   if (fused && L > 0 && i % (n_q / n_v) == 0 && tid < LPR)
@@ -560,30 +588,25 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
   const int nr = (L + range_rows - 1) / range_rows;
   const int n_c = nr == 0 ? 0 : (nr - 1) * top_k + min(top_k, L - (nr - 1) * range_rows);
   const int kk = min(top_k, L);
-  const float* cs = cand_s + head * n_ranges * top_k;
-  const int32_t* ci = cand_i + head * n_ranges * top_k;
   const bool in_regs = n_c <= E * kSelThreads;
-  float s[E];
-  int32_t idx[E];
   if (in_regs) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int p = reg_index<E>(e);
-      s[e] = p < n_c ? cs[p] : -INFINITY;
-      idx[e] = p < n_c ? ci[p] : 0;
+      if (reg_index<E>(e) >= n_c) {
+        s[e] = -INFINITY;
+        idx[e] = 0;
+      }
     }
   }
 
   clear_hists(hist);
   // Softmax normaliser over all L rows from the ranges' (max, sum); every
   // wave computes it alike, so no barrier is needed.
-  const float* ml = range_ml + head * n_ranges * 2;
-  const int lane = tid & 63;
-  float M = -INFINITY;
-  for (int r = lane; r < nr; r += 64) M = fmaxf(M, ml[2 * r]);
+  float M = lane < nr ? ml_m : -INFINITY;
+  for (int r = lane + 64; r < nr; r += 64) M = fmaxf(M, ml[2 * r]);
   M = wave_max(M);
-  float Z = 0.f;
-  for (int r = lane; r < nr; r += 64) Z += fast_exp2(ml[2 * r] - M) * ml[2 * r + 1];
+  float Z = lane < nr ? fast_exp2(ml_m - M) * ml_l : 0.f;
+  for (int r = lane + 64; r < nr; r += 64) Z += fast_exp2(ml[2 * r] - M) * ml[2 * r + 1];
   Z = wave_sum(Z);
   const float invZ = L > 0 ? 1.f / Z : 0.f;
   __syncthreads();  // histograms cleared
