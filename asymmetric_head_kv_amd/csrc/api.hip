@@ -26,10 +26,11 @@ constexpr int kMaxChunks = 8192;      // bounds the workspace and the combine's 
 // device), and when they differ the chunks past a short sequence's end are
 // empty, so with one planned round many CU slots would sit idle.  With more,
 // smaller chunks the dispatcher refills them (16 sequences of 4k..32k rows:
-// 276 -> 253 us; uniform 4 x 64k loses 3% at that chunk length, so small
-// batches keep one round).
+// 276 us at one round, 254 us at 8x (512-row chunks), 238 us at 7x (640-row
+// chunks; 448 and 768 rows time alike, 512 and 1024 slower); uniform
+// 4 x 64k loses 3% at such chunk lengths, so small batches keep one round).
 constexpr int kRaggedBatch = 8;
-constexpr int kRaggedOversub = 8;
+constexpr int kRaggedOversub = 7;
 constexpr int kMinChunk = 64;
 
 bool is_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
