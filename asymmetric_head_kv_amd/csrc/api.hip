@@ -126,10 +126,15 @@ struct SelLayout {
 };
 
 // Rows per logit-kernel workgroup (four waves, one 64-row tile each per
-// step): one tile per wave while that needs at most 8192 waves, more beyond.
+// step): one tile per wave while that needs at most 4096 waves, more beyond;
+// batches of kRaggedBatch or more sequences aim at 16384 waves, since chunks
+// past a short sequence's end are empty (4 x 64k: 51.7 -> 50.4 us per
+// selective step at 1024-row chunks; 16 sequences of 4k..32k rows:
+// 80.7 -> 74.5 us at 512-row chunks).
 int plan_score_chunk(int n_k, int batch, int max_ctx) {
   const long long tiles = ((long long)max_ctx + 63) / 64 * n_k * batch;
-  long long tpw = (tiles + 8191) / 8192;
+  const long long target = batch >= kRaggedBatch ? 16384 : 4096;
+  long long tpw = (tiles + target - 1) / target;
   if (tpw < 1) tpw = 1;
   if (tpw > (1 << 20)) tpw = 1 << 20;
   return (int)(256 * tpw);
