@@ -145,11 +145,57 @@ def prefill(q, k_cache, v_cache, ctx_len, scale: float | None = None,
     lse = np.full((B, T, n_q), np.nan, dtype=np.float64)
     for b, r in rows:
         p = int(ctx_len[b]) - T + r
+        n_vis = max(p + 1, 0)      # keys 0..p; none when the row sits before key 0
         for i in range(n_q):
             g = group_sharing_index(i, n_q, n_k)
             hv = group_sharing_index(i, n_q, n_v)
             out[b, r, i], lse[b, r, i] = attend_one(
-                q[b, r, i], k_cache[b, g, :p + 1], v_cache[b, hv, :p + 1], scale)
+                q[b, r, i], k_cache[b, g, :n_vis], v_cache[b, hv, :n_vis], scale)
+    return out, lse
+
+
+def prefill_all_rows(q, k_cache, v_cache, ctx_len, scale: float | None = None):
+    """Every row of :func:`prefill`, with one matrix product per head.
+
+    The same definition written over all new rows of a (sequence, query
+    head) at once: S = scale * Q_i K_g^T over the L_b cache rows (t_new x
+    L_b), score (r, j) dropped (set to -inf) when key j lies past row r's
+    position p_r = L_b - t_new + r, then per row the two-pass softmax of
+    :func:`attention_weights` (row maximum, exponentials, normalisation) and
+    the weighted sum W V (section 3.4 Steps 4 and 5, row by row).  Rows with
+    p_r < 0 see no key: o = 0, lse = -inf.  numpy's matrix product is the
+    only library step; it trades the per-row loop for memory (two t_new x
+    L_b float64 matrices per head), which makes full-size prefills feasible.
+    Returns ``(out[B][t_new][n_q][d_v], lse[B][t_new][n_q])`` in float64.
+    """
+    B, T, n_q, d_k = q.shape
+    n_k = k_cache.shape[1]
+    n_v, d_v = v_cache.shape[1], v_cache.shape[3]
+    if scale is None:
+        scale = default_scale(d_k)
+    out = np.zeros((B, T, n_q, d_v), dtype=np.float64)
+    lse = np.full((B, T, n_q), -math.inf, dtype=np.float64)
+    for b in range(B):
+        L = int(ctx_len[b])
+        p = L - T + np.arange(T)              # position of each new row
+        seen = p >= 0                         # rows that see at least key 0
+        if not seen.any():
+            continue
+        # visible[r, j]: key j at or before row r's position.
+        visible = np.arange(L)[None, :] <= p[:, None]
+        for i in range(n_q):
+            g = group_sharing_index(i, n_q, n_k)
+            hv = group_sharing_index(i, n_q, n_v)
+            Q = np.asarray(q[b, :, i, :], dtype=np.float64)
+            K = np.asarray(k_cache[b, g, :L], dtype=np.float64)
+            V = np.asarray(v_cache[b, hv, :L], dtype=np.float64)
+            S = scale * (Q @ K.T)
+            S[~visible] = -math.inf
+            m = S[seen].max(axis=1, keepdims=True)
+            W = np.exp(S[seen] - m)
+            Z = W.sum(axis=1)
+            out[b, seen, i] = (W @ V) / Z[:, None]
+            lse[b, seen, i] = m[:, 0] + np.log(Z)
     return out, lse
 
 

@@ -301,6 +301,42 @@ def test_prefill_row_subset():
     assert np.isnan(part[0, :3]).all()
 
 
+def test_prefill_all_rows_equals_row_by_row():
+    # The matrix form over all new rows of a head against the row-by-row
+    # definition: a ragged batch whose second sequence is shorter than the
+    # prefill (its first rows see no key), asymmetric heads, both head maps.
+    B, T = 3, 7
+    n_q, n_k, n_v, d_k, d_v = 8, 2, 4, 16, 24
+    qp = _rand(21, B, T, n_q, d_k)
+    _, k, v, _ = _case(22, B, n_q, n_k, n_v, d_k, d_v, 40)
+    lens = np.array([40, 4, 7])
+    ref, ref_lse = oracle.prefill(qp, k, v, lens, 0.3)
+    out, lse = oracle.prefill_all_rows(qp, k, v, lens, 0.3)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+    assert (out[1, :3] == 0).all() and np.isneginf(lse[1, :3]).all()
+
+
+def test_prefill_all_rows_matches_masked_sdpa():
+    # An independent library routine: torch's scaled_dot_product_attention in
+    # fp64 with an explicit bottom-right causal mask (row r of T sees keys
+    # 0 .. L - T + r) on K / V heads repeated to the query heads.
+    B, T, L = 1, 9, 25
+    n_q, n_k, n_v, d_k, d_v = 8, 2, 8, 32, 16
+    qp = _rand(23, B, T, n_q, d_k)
+    _, k, v, _ = _case(24, B, n_q, n_k, n_v, d_k, d_v, L)
+    out, lse = oracle.prefill_all_rows(qp, k, v, np.array([L]))
+    kx = torch.from_numpy(k[0][[i * n_k // n_q for i in range(n_q)]])
+    vx = torch.from_numpy(v[0][[i * n_v // n_q for i in range(n_q)]])
+    qt = torch.from_numpy(qp[0]).transpose(0, 1).contiguous()      # [n_q][T][d_k]
+    mask = torch.arange(L)[None, :] <= (L - T + torch.arange(T))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kx, vx, attn_mask=mask)
+    np.testing.assert_allclose(out[0], ref.transpose(0, 1).numpy(), rtol=0, atol=1e-12)
+    s = (qt @ kx.transpose(1, 2)) / math.sqrt(d_k)
+    ref_lse = torch.logsumexp(s.masked_fill(~mask, -math.inf), dim=-1)
+    np.testing.assert_allclose(lse[0], ref_lse.transpose(0, 1).numpy(), rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- kv_append
 
 def test_kv_append_is_step2_concatenation():
@@ -341,10 +377,13 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         lambda g: test_prefill_causal_mask(),
         lambda g: test_default_scale_is_inverse_sqrt_dk(),
         lambda g: test_zero_scale_is_mean_of_value_rows(),
+        lambda g: test_prefill_all_rows_equals_row_by_row(),
+        lambda g: test_prefill_all_rows_matches_masked_sdpa(),
     ]
     from conftest import read_golden
 
     real_gsi, real_weights, real_prefill = A.group_sharing_index, A.attention_weights, A.prefill
+    real_all_rows = A.prefill_all_rows
 
     def ceil_map(i, n_q, n_h):
         return -((-int(i) * int(n_h)) // int(n_q))
@@ -363,6 +402,15 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     def strict_causal(q, k_cache, v_cache, ctx_len, scale=None, rows=None):
         return real_prefill(q, k_cache, v_cache, np.asarray(ctx_len) - 1, scale, rows)
 
+    def all_rows_strict_causal(q, k_cache, v_cache, ctx_len, scale=None):
+        return real_all_rows(q, k_cache, v_cache, np.asarray(ctx_len) - 1, scale)
+
+    def all_rows_top_left(q, k_cache, v_cache, ctx_len, scale=None):
+        # causal mask aligned to the first key instead of the newest row
+        T = q.shape[1]
+        o, l = real_all_rows(q, k_cache, v_cache, np.full(len(ctx_len), T), scale)
+        return o, l
+
     mutants = {
         "ceil head map": ("group_sharing_index", ceil_map),
         "round-robin head map": ("group_sharing_index", lambda i, n_q, n_h: int(i) % int(n_h)),
@@ -370,6 +418,8 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         "weights not normalised": ("attention_weights", unnormalised),
         "scale 1/sqrt(d_v)": ("default_scale", dv_scale),
         "causal off by one": ("prefill", strict_causal),
+        "all-rows causal off by one": ("prefill_all_rows", all_rows_strict_causal),
+        "all-rows top-left causal mask": ("prefill_all_rows", all_rows_top_left),
     }
     for name, (attr, fn) in mutants.items():
         with monkeypatch.context() as m:
