@@ -9,13 +9,13 @@ Tensor layouts (contiguous, on one GPU):
   k_cache      [B, n_k, l_cap, d_k]     v_cache      [B, n_v, l_cap, d_v]
   k_new        [B, t_new, n_k, d_k]     v_new        [B, t_new, n_v, d_v]
   ctx_len, pos int32 [B]
-dtype float32 or bfloat16 (prefill: bfloat16).
+dtype float32 or bfloat16 (prefill: bfloat16).  ``scale=None`` passes 0, which
+the library reads as its default 1/sqrt(d_k).
 """
 
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -199,7 +199,7 @@ def decode(q, k_cache, v_cache, ctx_len, *, max_ctx=None, scale=None, out=None,
     if k_new is not None and (k_new.numel() != B * n_k * d_k or v_new.numel() != B * n_v * d_v):
         raise ValueError("k_new must hold [B, n_k, d_k] and v_new [B, n_v, d_v]")
     max_ctx = l_cap if max_ctx is None else int(max_ctx)
-    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    scale = 0.0 if scale is None else float(scale)  # 0: the library's 1/sqrt(d_k)
     if out is None:
         out = torch.empty((B, n_q, d_v), dtype=q.dtype, device=q.device)
     elif out.shape != (B, n_q, d_v) or out.dtype != q.dtype:
@@ -257,7 +257,7 @@ def decode_selective(q, k_cache, v_cache, ctx_len, *, top_k=100, max_ctx=None, s
     if k_new is not None and (k_new.numel() != B * n_k * d_k or v_new.numel() != B * n_v * d_v):
         raise ValueError("k_new must hold [B, n_k, d_k] and v_new [B, n_v, d_v]")
     max_ctx = l_cap if max_ctx is None else int(max_ctx)
-    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    scale = 0.0 if scale is None else float(scale)  # 0: the library's 1/sqrt(d_k)
     top_k = int(top_k)
     if out is None:
         out = torch.empty((B, n_q, d_v), dtype=q.dtype, device=q.device)
@@ -332,7 +332,7 @@ def decode_paged(q, k_pages, v_pages, block_table, ctx_len, *, max_ctx=None, sca
     if k_new is not None and (k_new.numel() != B * n_k * d_k or v_new.numel() != B * n_v * d_v):
         raise ValueError("k_new must hold [B, n_k, d_k] and v_new [B, n_v, d_v]")
     max_ctx = max_blocks * P if max_ctx is None else int(max_ctx)
-    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    scale = 0.0 if scale is None else float(scale)  # 0: the library's 1/sqrt(d_k)
     if out is None:
         out = torch.empty((B, n_q, d_v), dtype=q.dtype, device=q.device)
     elif out.shape != (B, n_q, d_v) or out.dtype != q.dtype:
@@ -433,7 +433,7 @@ def prefill(q, k_cache, v_cache, ctx_len, *, scale=None, out=None, lse=None,
         raise ValueError("ctx_len must be int32 [B]")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q and the caches must share one dtype")
-    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    scale = 0.0 if scale is None else float(scale)  # 0: the library's 1/sqrt(d_k)
     if out is None:
         out = torch.empty((B, T, n_q, d_v), dtype=q.dtype, device=q.device)
     elif out.shape != (B, T, n_q, d_v) or out.dtype != q.dtype:
@@ -466,7 +466,7 @@ def prefill_paged(q, k_pages, v_pages, block_table, ctx_len, *, scale=None, out=
         raise ValueError("ctx_len must be int32 [B]")
     if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise TypeError("q and the page pools must share one dtype")
-    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    scale = 0.0 if scale is None else float(scale)  # 0: the library's 1/sqrt(d_k)
     if out is None:
         out = torch.empty((B, T, n_q, d_v), dtype=q.dtype, device=q.device)
     elif out.shape != (B, T, n_q, d_v) or out.dtype != q.dtype:
@@ -507,7 +507,7 @@ def decode_selective_paged(q, k_pages, v_pages, block_table, ctx_len, *, top_k=1
     if k_new is not None and (k_new.numel() != B * n_k * d_k or v_new.numel() != B * n_v * d_v):
         raise ValueError("k_new must hold [B, n_k, d_k] and v_new [B, n_v, d_v]")
     max_ctx = max_blocks * P if max_ctx is None else int(max_ctx)
-    scale = 1.0 / math.sqrt(d_k) if scale is None else float(scale)
+    scale = 0.0 if scale is None else float(scale)  # 0: the library's 1/sqrt(d_k)
     top_k = int(top_k)
     if out is None:
         out = torch.empty((B, n_q, d_v), dtype=q.dtype, device=q.device)

@@ -86,6 +86,20 @@ int chunks_for(int max_ctx, int S) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The softmax scale a call uses: 0 selects the default 1/sqrt(d_k), the
+// divisor of the attention scores in section 3.4 Step 4 of the Sigma
+// architecture page; any other value must be positive and finite.  Returns
+// false for a rejected value.
+bool resolve_scale(float scale, int d_k, float* out) {
+  if (scale == 0.f) {
+    *out = 1.f / sqrtf((float)d_k);
+    return true;
+  }
+  if (!(scale > 0.f) || !isfinite(scale)) return false;
+  *out = scale;
+  return true;
+}
+
 constexpr int kPrefillRows = 128;  // query rows per prefill workgroup
 
 // Key splits for a prefill: enough workgroups for two per CU (the kernel's
@@ -250,7 +264,7 @@ static int prepare_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, in
   if (st) return st;
   if (batch < 0 || l_cap < 0 || max_ctx < 0 || max_ctx > l_cap || batch > 65535)
     return DQKV_ERR_SHAPE;
-  if (need_qkv && (!(scale > 0.f) || !isfinite(scale))) return DQKV_ERR_SHAPE;
+  if (need_qkv && !resolve_scale(scale, d_k, &scale)) return DQKV_ERR_SHAPE;
   if (need_qkv && (!q || !k_cache || !v_cache)) return DQKV_ERR_NULL;
   if (need_out && !out) return DQKV_ERR_NULL;
   if (!ctx_len || !workspace) return DQKV_ERR_NULL;
@@ -390,7 +404,7 @@ static int run_prefill(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32
   if (dtype != DQKV_BF16) return DQKV_ERR_UNSUPPORTED;
   if ((d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128)) return DQKV_ERR_UNSUPPORTED;
   if (batch < 0 || t_new < 0 || l_cap < 0 || batch > 65535) return DQKV_ERR_SHAPE;
-  if (!(scale > 0.f) || !isfinite(scale)) return DQKV_ERR_SHAPE;
+  if (!resolve_scale(scale, d_k, &scale)) return DQKV_ERR_SHAPE;
   if (batch == 0 || t_new == 0) return DQKV_OK;
   if (!q || !k_cache || !v_cache || !ctx_len || !out) return DQKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
@@ -473,7 +487,7 @@ static int run_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int
   if (batch < 0 || l_cap < 0 || max_ctx < 0 || max_ctx > l_cap || batch > 65535 ||
       n_q > 65535)
     return DQKV_ERR_SHAPE;
-  if (!(scale > 0.f) || !isfinite(scale)) return DQKV_ERR_SHAPE;
+  if (!resolve_scale(scale, d_k, &scale)) return DQKV_ERR_SHAPE;
   SelLayout lay;
   st = selective_layout(n_q, n_k, batch, max_ctx, top_k, &lay);
   if (st) return st;

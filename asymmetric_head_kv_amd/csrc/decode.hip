@@ -79,8 +79,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i0 = (quad * 4 + wave) * H;   // this wave's first query head
   if (i0 >= n_q) return;
-  int L = ctx_len[b];
-  L = max(0, min(L, min(max_ctx, l_cap)));
+  const int L_raw = ctx_len[b];
+  const int L = max(0, min(L_raw, min(max_ctx, l_cap)));
   const int j0 = c * S;
   if (j0 >= L) return;
   const int rows = min(S, L - j0);
@@ -103,12 +103,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   }
 
   const int vl = lane % LPR_V, vr = lane / LPR_V;
+  // Page of the tile at chunk row t0: the raw table entry, and the entry
+  // clamped into [0, num_pages) that reads use.
+  auto page_raw = [&](int t0) -> int {
+    return pm.table[(size_t)b * pm.max_blocks + ((j0 + t0) >> pm.page_shift)];
+  };
+  auto page_of = [&](int t0) -> size_t {
+    return (size_t)min(max(page_raw(t0), 0), pm.num_pages - 1);
+  };
   // Address of row 0 of the 64-row tile that starts at chunk row t0 (this
   // lane's slice of it), for K and for V.
-  auto page_of = [&](int t0) -> size_t {
-    const int blk = pm.table[(size_t)b * pm.max_blocks + ((j0 + t0) >> pm.page_shift)];
-    return (size_t)min(max(blk, 0), pm.num_pages - 1);
-  };
   auto k_tile = [&](auto* base, int t0, size_t page) {
     if constexpr (PAGED)
       return base + ((page * n_k + hk) * ((size_t)1 << pm.page_shift) +
@@ -130,17 +134,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   // group in the K and V load patterns), so each lane reads back its own
   // store: program order, with kc / kc_w and vc / vc_w possibly aliasing as
   // far as the compiler knows.  Only this chunk touches row L - 1.
-  if (k_new != nullptr && L - 1 - j0 < rows) {
+  // Nothing is stored when the length lies outside [1, min(max_ctx, l_cap)]
+  // (it is clamped for reading, and row L - 1 then holds history that must
+  // survive) or, paged, when the row's table entry names no page: such rows
+  // are skipped, as kv_append skips them.
+  if (k_new != nullptr && L_raw == L && L - 1 - j0 < rows) {
     const int r_new = L - 1 - j0;
     const int t_new0 = r_new & ~63;  // tile holding the new row
-    const size_t pg = PAGED ? page_of(t_new0) : 0;
-    const int in_tile = r_new - t_new0;
-    if (kr == in_tile % RPL_K)
-      *reinterpret_cast<u32x4*>(k_tile(kc_w, t_new0, pg) + (size_t)in_tile * DK) =
-          load16(k_new + ((size_t)b * n_k + hk) * DK + kl * EPL);
-    if (vr == in_tile % RPL_V)
-      *reinterpret_cast<u32x4*>(v_tile(vc_w, t_new0, pg) + (size_t)in_tile * DV) =
-          load16(v_new + ((size_t)b * n_v + hv) * DV + vl * EPL);
+    const int blk = PAGED ? page_raw(t_new0) : 0;
+    if (!PAGED || (blk >= 0 && blk < pm.num_pages)) {
+      const size_t pg = (size_t)blk;
+      const int in_tile = r_new - t_new0;
+      if (kr == in_tile % RPL_K)
+        *reinterpret_cast<u32x4*>(k_tile(kc_w, t_new0, pg) + (size_t)in_tile * DK) =
+            load16(k_new + ((size_t)b * n_k + hk) * DK + kl * EPL);
+      if (vr == in_tile % RPL_V)
+        *reinterpret_cast<u32x4*>(v_tile(vc_w, t_new0, pg) + (size_t)in_tile * DV) =
+            load16(v_new + ((size_t)b * n_v + hv) * DV + vl * EPL);
+    }
   }
 
   // The lane keeps the score of tile row my_row = kl * RPL_K + kr (K load kl,

@@ -12,9 +12,10 @@
 // barrier, before any wave reads that buffer; vector-memory loads complete
 // in issue order, so vmcnt(n) leaves only the n most recent in flight.
 // The LDS address must be wave-uniform (it is taken from the first lane).
-// The s_nop covers the wait state a transfer needs after m0 is written; m0
-// holds no compiler value across these statements in the kernels that use
-// them (they issue no other m0-using instruction).
+// m0 (which the compiler may use for its own purposes and does not save
+// around inline asm) is copied to a scratch SGPR, set for the transfer and
+// restored in the same statement; the s_nop covers the wait state a
+// transfer needs after m0 is written.
 #pragma once
 
 #include <stdint.h>
@@ -23,17 +24,19 @@ namespace dqkv {
 
 typedef __attribute__((address_space(3))) void lds_dma_t;
 
-// m0 is listed as clobbered for the reader; the compiler warns that it does
-// not preserve reserved registers around asm, which is moot here (see above:
-// no compiler value lives in m0 in these kernels).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-
 // 64-bit per-lane source address.
 __device__ __forceinline__ void dma16(const void* g, lds_dma_t* l) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)l);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(m) : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(m)
+      : "memory");
 }
 
 // Wave-uniform base (moved to scalar registers) plus a 32-bit per-lane byte
@@ -46,10 +49,17 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, lds_dma_
   const uint64_t a = (uint64_t)base;
   const uint64_t su = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"((const void*)su), "s"(m) : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"((const void*)su), "s"(m)
+      : "memory");
 }
-
-#pragma clang diagnostic pop
 
 }  // namespace dqkv

@@ -54,6 +54,19 @@ __device__ __forceinline__ T* cache_row(T* c, const PageMap& pm, int b, int H, i
   return c + (((size_t)b * H + h) * l_cap + j) * D;
 }
 
+// Row j as a store destination: as cache_row, but a page-table entry outside
+// [0, num_pages) gives nullptr and the row is not written (a read may clamp;
+// a write there would land in another sequence's page).
+template <typename T, int D>
+__device__ __forceinline__ T* cache_row_store(T* c, const PageMap& pm, int b, int H, int h,
+                                              int l_cap, int j) {
+  if (pm.table != nullptr) {
+    const int blk = pm.table[(size_t)b * pm.max_blocks + (j >> pm.page_shift)];
+    if (blk < 0 || blk >= pm.num_pages) return nullptr;
+  }
+  return cache_row<T, D>(c, pm, b, H, h, l_cap, j);
+}
+
 __device__ __forceinline__ uint64_t lanes_below() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -311,8 +324,8 @@ __global__ __launch_bounds__(256) void sel_score_kernel(
   const int G = n_q / n_k, slices = G / HW;
   const int hk = blockIdx.y / slices, slice = blockIdx.y % slices;
   const int i0 = hk * G + slice * HW;
-  int L = ctx_len[b];
-  L = max(0, min(L, min(max_ctx, l_cap)));
+  const int L_raw = ctx_len[b];
+  const int L = max(0, min(L_raw, min(max_ctx, l_cap)));
   const int j0 = c * S;
   if (j0 >= L) return;
   const int rows = min(S, L - j0);
@@ -326,12 +339,15 @@ __global__ __launch_bounds__(256) void sel_score_kernel(
     for (int e = 0; e < EPL; ++e) qf[h][e] *= qscale;
   }
 
-  const bool fused = k_new != nullptr;
+  // Fused append only for a length inside [1, min(max_ctx, l_cap)] (a longer
+  // one is clamped for reading and row L - 1 keeps its history).
+  const bool fused = k_new != nullptr && L_raw == L;
   const int r_new = fused ? L - 1 - j0 : -1;  // in [0, rows) iff this chunk owns it
   const T* kn = fused ? k_new + ((size_t)b * n_k + hk) * DK + kl * EPL : nullptr;
-  if (fused && r_new < rows && slice == 0 && wave == (r_new / 64) % 4 && lane < LPR_K)
-    *reinterpret_cast<u32x4*>(cache_row<T, DK>(kc_w, pm, b, n_k, hk, l_cap, L - 1) +
-                              kl * EPL) = load16(kn);
+  if (fused && r_new < rows && slice == 0 && wave == (r_new / 64) % 4 && lane < LPR_K) {
+    if (T* dst = cache_row_store<T, DK>(kc_w, pm, b, n_k, hk, l_cap, L - 1))
+      *reinterpret_cast<u32x4*>(dst + kl * EPL) = load16(kn);
+  }
 
   float* out = scores + ((size_t)b * n_q + i0) * ld_s + j0;
   const int my_row = kl * RPL_K + kr;
@@ -390,8 +406,8 @@ __global__ __launch_bounds__(256) void sel_score_mfma_kernel(
   const int hk = blockIdx.y / slices, slice = blockIdx.y % slices;
   const int h0 = slice * 16, nh = min(16, G - h0);
   const int i0 = hk * G + h0;
-  int L = ctx_len[b];
-  L = max(0, min(L, min(max_ctx, l_cap)));
+  const int L_raw = ctx_len[b];
+  const int L = max(0, min(L_raw, min(max_ctx, l_cap)));
   const int j0 = c * S;
   if (j0 >= L) return;
   const int rows = min(S, L - j0);
@@ -404,12 +420,15 @@ __global__ __launch_bounds__(256) void sel_score_mfma_kernel(
         sel_bf16x8, l16 < nh ? load16(q + ((size_t)b * n_q + i0 + l16) * DK + kb * 32 + 8 * kg)
                              : u32x4{0u, 0u, 0u, 0u});
 
-  const bool fused = k_new != nullptr;
+  // Fused append only for a length inside [1, min(max_ctx, l_cap)].
+  const bool fused = k_new != nullptr && L_raw == L;
   const int r_new = fused ? L - 1 - j0 : -1;  // in [0, rows) iff this chunk owns it
   const bf16* kn = fused ? k_new + ((size_t)b * n_k + hk) * DK + 8 * kg : nullptr;
-  if (fused && r_new < rows && slice == 0 && wave == (r_new / 64) % 4 && lane < DK / 8)
-    *reinterpret_cast<u32x4*>(cache_row<bf16, DK>(kc_w, pm, b, n_k, hk, l_cap, L - 1) +
-                              8 * lane) = load16(k_new + ((size_t)b * n_k + hk) * DK + 8 * lane);
+  if (fused && r_new < rows && slice == 0 && wave == (r_new / 64) % 4 && lane < DK / 8) {
+    if (bf16* dst = cache_row_store<bf16, DK>(kc_w, pm, b, n_k, hk, l_cap, L - 1))
+      *reinterpret_cast<u32x4*>(dst + 8 * lane) =
+          load16(k_new + ((size_t)b * n_k + hk) * DK + 8 * lane);
+  }
 
   float* out = scores + ((size_t)b * n_q + i0 + l16) * ld_s + j0;
   for (int t0 = wave * 64; t0 < rows; t0 += 256) {
@@ -554,7 +573,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
 
   const int i = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
-  int L = ctx_len[b];
+  const int L_raw = ctx_len[b];
+  int L;
   const size_t head = (size_t)b * n_q + i;
   // The candidate slots and the ranges' (max, sum) are requested together
   // with the sequence length (all n_ranges slots of the head exist in the
@@ -574,13 +594,15 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
   }
   const float ml_m = lane < n_ranges ? ml[2 * lane] : -INFINITY;
   const float ml_l = lane < n_ranges ? ml[2 * lane + 1] : 0.f;
-  L = max(0, min(L, min(max_ctx, l_cap)));
+  L = max(0, min(L_raw, min(max_ctx, l_cap)));
   const int hv = (i * n_v) / n_q;
-  const bool fused = v_new != nullptr;
+  // Fused append only for a length inside [1, min(max_ctx, l_cap)].
+  const bool fused = v_new != nullptr && L_raw == L && L > 0;
   const T* vn = fused ? v_new + ((size_t)b * n_v + hv) * DV : nullptr;
-  if (fused && L > 0 && i % (n_q / n_v) == 0 && tid < LPR)
-    *reinterpret_cast<u32x4*>(cache_row<T, DV>(vc_w, pm, b, n_v, hv, l_cap, L - 1) +
-                              tid * EPL) = load16(vn + tid * EPL);
+  if (fused && i % (n_q / n_v) == 0 && tid < LPR) {
+    if (T* dst = cache_row_store<T, DV>(vc_w, pm, b, n_v, hv, l_cap, L - 1))
+      *reinterpret_cast<u32x4*>(dst + tid * EPL) = load16(vn + tid * EPL);
+  }
 
   // Candidates: range r contributed min(top_k, rows of r) entries at
   // [r * top_k, ...); all ranges but the last are full, so the n_c entries

@@ -65,6 +65,11 @@ def parse():
     p.add_argument("--no-compat", action="store_true",
                    help="skip the kv_group_sharing leg")
     p.add_argument("--no-augq", action="store_true", help="skip the augmented-Q leg")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="skip the other decode workloads (64k x 4 at d_k 64 / 128 and "
+                        "symmetric, the ragged batch, the tiny fp32 case)")
+    p.add_argument("--no-ket", action="store_true",
+                   help="skip the KET replica (SIGMA-1.5B vs standard GQA, prefixes 2k-32k)")
     p.add_argument("--kernel-only", action="store_true",
                    help="only run steps (for profilers); skip twin, prefill, CPU baseline")
     p.add_argument("--ket", action="store_true",
@@ -86,6 +91,11 @@ def kv_elements_per_token(n_k: int, d_k: int, n_v: int, d_v: int) -> int:
 
 TWINS = {"decode32k_asym": "decode32k_sym", "decode64k_dk64": "decode64k_sym",
          "decode64k_dk128": "decode64k_sym"}
+
+# Decode workloads measured beside the headline one in the default run (each
+# is also a full-size parity case of the GPU tests).
+OTHER_WORKLOADS = ("decode64k_dk64", "decode64k_dk128", "decode64k_sym", "ragged16",
+                   "tiny_f32")
 
 
 # ----------------------------------------------------------------- device side
@@ -416,6 +426,32 @@ def pmc_traffic(workload: str):
         return None
 
 
+def decode_record(name: str, steps: int, warmup: int, chunk: int = 0) -> dict:
+    """Step time (split with the fused append + combine, graph replay over
+    cache replicas) and the split kernel alone, for one decode workload."""
+    bn = DecodeBench(name, chunk)
+    ms, graphed = bn.time_steps(steps, warmup)
+    split_ms, comb_ms = bn.time_kernels(steps)
+    n_q, n_k, n_v, d_k, d_v = bn.shape
+    gbs = bn.alg_bytes_step / (ms * 1e-3) / 1e9
+    split_gbs = bn.alg_bytes_split / (split_ms * 1e-3) / 1e9
+    rec = {"us_per_step": round(ms * 1e3, 2), "GBps": round(gbs, 1),
+           "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "us_per_step_spread": bn.step_pct_us,
+           "alg_bytes_per_step": bn.alg_bytes_step,
+           "split_us": round(split_ms * 1e3, 2), "combine_us": round(comb_ms * 1e3, 2),
+           "split_GBps": round(split_gbs, 1),
+           "split_frac_of_hbm_peak": round(split_gbs / HBM_PEAK_GBS, 4),
+           "dtype": bn.case.dtype,
+           "shape": {"batch": bn.B, "max_ctx": bn.max_ctx, "ctx_sum": int(bn.ctx.sum()),
+                     "n_q": n_q, "n_k": n_k, "n_v": n_v, "d_k": d_k, "d_v": d_v},
+           "chunk_rows": bn.S, "cache_replicas": bn.replicas,
+           "timing": "hip graph replay" if graphed else "eager launches"}
+    bn.free()
+    del bn
+    return rec
+
+
 def ket_replica(steps: int):
     """Split- and combine-kernel times (each timed alone, graph replay) and
     their sum, for SIGMA-1.5B vs the standard GQA shape, with the relative
@@ -572,35 +608,102 @@ def hbm_copy_gbs(nbytes: int = 2 << 30, reps: int = 10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(name: str, seconds: float):
-    """The fp64 oracle on the same workload, timed on the host cores."""
+def _cpu_threads() -> int:
+    """Worker threads for the oracle: the host's CPUs, at most 16 (one GPU's
+    share of a host)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _oracle_units(name: str):
+    """The workload as independent oracle calls: one (sequence, query head)
+    decode per unit, or one prefill row (all query heads) per unit.  Returns
+    (units, algorithmic bytes or flops of the whole step, unit name, metric
+    unit)."""
     import numpy as np
 
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
-    except Exception:
-        threads = 1
     case = synth.make_case(**synth.workload(name))
-    q, k, v = case.widened()
+    # Widened once to float64 (exact), so each call reads its rows as they
+    # are instead of converting them again.
+    q, k, v = (x.astype(np.float64) for x in case.widened())
     ctx = np.asarray(case.ctx_len)
     esize = 2 if case.dtype == "bf16" else 4
-    byts = int(ctx.sum()) * kv_elements_per_token(case.n_k, case.d_k, case.n_v, case.d_v) * esize
-    n = 0
+    if case.t_new:
+        T = case.t_new
+        rows = list(range(T))
+        units = [lambda r=r: oracle.prefill(q, k, v, ctx, case.scale, rows=[(0, r)])
+                 for r in rows]
+        pairs = sum(int(ctx[0]) - T + r + 1 for r in rows)
+        work = pairs * case.n_q * 2 * (case.d_k + case.d_v)
+        return units, work, "prefill row (all query heads)", "GFLOP/s"
+    units = []
+    for b in range(case.batch):
+        L = int(ctx[b])
+        for i in range(case.n_q):
+            g = oracle.group_sharing_index(i, case.n_q, case.n_k)
+            hv = oracle.group_sharing_index(i, case.n_q, case.n_v)
+            units.append(lambda b=b, i=i, g=g, hv=hv, L=L: oracle.attend_one(
+                q[b, i], k[b, g, :L], v[b, hv, :L], case.scale))
+    work = int(ctx.sum()) * kv_elements_per_token(case.n_k, case.d_k, case.n_v, case.d_v) * esize
+    return units, work, "(sequence, query head) decode", "GB/s"
+
+
+def cpu_baseline_one(name: str, seconds: float, threads: int) -> dict:
+    """The fp64 oracle, unchanged, on a bounded sample of one workload: its
+    independent units (evenly spread over the step) run on `threads` host
+    threads until about `seconds` have passed; the full step's time is the
+    unit count over the measured unit rate."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    units, work, unit_name, unit = _oracle_units(name)
+    n = len(units)
+    # Units in a strided order, so a partial sample spreads over the step
+    # (prefill rows grow with their position); whole passes repeat while
+    # time is left.
+    stride = max(1, n // 16)
+    order = [u for r in range(stride) for u in range(r, n, stride)]
+    done = 0
     t0 = time.perf_counter()
-    while True:
-        oracle.decode(q, k, v, ctx, case.scale)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    per = el / n
-    return {"value": round(byts / per / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "us_per_step": round(per * 1e6, 1),
-            "sample": f"{n} full decode steps of {name} (fp64 numpy oracle, "
-                      f"{threads} BLAS threads, {el:.1f} s)"}
+    # One BLAS thread per worker: the workers are the parallelism.
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            batch = [units[order[(done + j) % n]] for j in range(threads)]
+            list(ex.map(lambda f: f(), batch))
+            done += len(batch)
+            if time.perf_counter() - t0 >= seconds:
+                break
+    el = time.perf_counter() - t0
+    step_s = el * n / done
+    scale = 1e9
+    rec = {"value": round(work / step_s / scale, 3), "unit": unit,
+           "us_per_step": round(step_s * 1e6, 1),
+           "sample": f"{done} unit calls ({unit_name}; {n} per step) in {el:.1f} s"}
+    return rec
+
+
+def cpu_baseline(name: str, seconds: float, per_config_seconds: float = 2.5,
+                 configs=()) -> dict:
+    """The fp64 oracle on the host cores: the headline workload, and a
+    bounded sample of every other configuration."""
+    threads = _cpu_threads()
+    main = cpu_baseline_one(name, seconds, threads)
+    out = {"value": main["value"], "unit": main["unit"], "cores": threads,
+           "host_cpus": os.cpu_count(), "kind": "oracle",
+           "us_per_step": main["us_per_step"],
+           "sample": f"{name}: {main['sample']}, on {threads} threads (fp64 numpy oracle; "
+                     f"step time = units / measured unit rate)"}
+    per = {}
+    for cfg in configs:
+        try:
+            per[cfg] = cpu_baseline_one(cfg, per_config_seconds, threads)
+        except Exception as e:  # a baseline, never the product: report and go on
+            per[cfg] = {"error": str(e)}
+        log(f"cpu baseline {cfg}: {per[cfg]}")
+    if per:
+        out["per_config"] = per
+    return out
 
 
 def main():
@@ -727,9 +830,31 @@ def main():
         if not args.no_augq:
             log("augmented Q")
             result["augq"] = augq_bench()
+        if not args.no_workloads:
+            recs = {}
+            for name in OTHER_WORKLOADS:
+                if name == args.workload:
+                    continue
+                log(f"workload {name}")
+                recs[name] = decode_record(name, args.steps, args.warmup, args.chunk)
+                log(f"  step {recs[name]['us_per_step']} us, split {recs[name]['split_us']} us")
+            sym = recs.get("decode64k_sym")
+            for name in ("decode64k_dk64", "decode64k_dk128"):
+                if sym and name in recs:
+                    r = recs[name]
+                    r["speedup_over_decode64k_sym"] = round(sym["us_per_step"] / r["us_per_step"], 3)
+                    r["byte_ratio_bound"] = round(sym["alg_bytes_per_step"] / r["alg_bytes_per_step"], 3)
+            result["workloads"] = recs
+        if not args.no_ket:
+            log("KET replica")
+            result["ket_replica"] = ket_replica(args.steps)
         if not args.no_cpu_baseline:
             log("cpu baseline (oracle)")
-            result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds)
+            cfgs = [c for c in ("tiny_f32", "decode32k_sym", "ragged16", "decode64k_dk64",
+                                "decode64k_dk128", "decode64k_sym", "prefill2k_on_30k")
+                    if c != args.workload]
+            result["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds,
+                                                  configs=cfgs)
     print(json.dumps(result), flush=True)
 
 

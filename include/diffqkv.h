@@ -16,8 +16,9 @@
  *
  *   o_i = sum_j softmax_j(scale * q_i . K_j) * V_j,   o_i in R^{d_v}
  *
- * (section 3.4 Steps 4 and 5), scale = 1/sqrt(d_k) unless the caller passes
- * another positive value.
+ * (section 3.4 Steps 4 and 5).  Every entry point that takes `scale` reads
+ * scale = 0 as the default 1/sqrt(d_k) (Step 4's divisor) and otherwise
+ * requires a positive finite value (DQKV_ERR_SHAPE).
  *
  * Memory layouts (row-major, innermost last; all device memory):
  *   q (decode)   [B][n_q][d_k]
@@ -125,8 +126,9 @@ int32_t kv_append(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
  *
  * max_ctx (host) bounds ctx_len and sizes the launch: 0 <= ctx_len[b] <=
  * max_ctx <= l_cap is required.  Values beyond are clamped to
- * min(max_ctx, l_cap) (memory-safe, result then covers only those rows).
- * ctx_len[b] = 0 yields out = 0 and lse = -inf.
+ * min(max_ctx, l_cap) (memory-safe, result then covers only those rows; the
+ * fused-append forms below then write nothing for that sequence, so the
+ * cache keeps its history).  ctx_len[b] = 0 yields out = 0 and lse = -inf.
  */
 int32_t diffqkv_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
                        int32_t d_v, int32_t dtype, int32_t batch,
@@ -296,9 +298,10 @@ int32_t diffqkv_decode_selective(int32_t n_q, int32_t n_k, int32_t n_v, int32_t 
  * page_rows is a power of two >= 64 (a 64-row decode tile then never spans
  * two pages, so each tile costs one table read).  The row capacity of a
  * sequence is max_blocks * page_rows.  Table entries outside
- * [0, num_pages) are not followed: kv_append_paged skips such rows and the
- * decode, prefill and selective paths clamp them into [0, num_pages) (a
- * wrong result for a malformed table, never an out-of-bounds access).
+ * [0, num_pages) are never written through: kv_append_paged and the fused
+ * appends of the decode and selective paths skip such rows, and their reads
+ * clamp the entry into [0, num_pages) (a wrong result for a malformed
+ * table, never an out-of-bounds access or a write into another page).
  *
  * kv_append_paged -- kv_append into a paged cache (pos, t_new, k_new, v_new
  *   as for kv_append; rows past the capacity are skipped).

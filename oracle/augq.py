@@ -5,10 +5,10 @@ import this module; the GPU library never calls it and it never calls the GPU
 library.
 
 Sigma architecture page, section 3.2 item 4 (Augmented Q with SwiGLU
-gating): the hidden state goes through two parallel projections, q_gate_proj
-and q_up_proj; the gate passes through the SwiGLU activation and multiplies
-the up projection element by element; q_down_proj maps the product to the
-query.  With weights in the usual (out, in) layout:
+gating).  In short: a gated two-branch projection widens the hidden state,
+the gate branch is activated and multiplies the other branch, and a third
+projection narrows the product back to the query width.  With weights in the
+usual (out, in) layout:
 
     g = h W_gate^T,  u = h W_up^T          (M x d_i; d_i = 3072 for SIGMA-1.5B)
     a = silu(g) * u,  silu(x) = x / (1 + e^{-x})

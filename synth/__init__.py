@@ -4,10 +4,12 @@ This module is the one piece shared by the fp64 oracle's tests and by the GPU
 path's tests and benchmark.  It draws random numbers and lays them out; it
 holds none of the attention arithmetic.
 
-Every tensor comes from its own PCG64 stream, keyed by ``(seed, stream id)``,
-so two layouts that share a tensor shape (for example the V cache of the
-asymmetric layout and of its symmetric twin) receive identical bytes, and a
-tensor of another shape (K, Q) is drawn from the same stream at its own size.
+Every tensor comes from its own PCG64 streams, keyed by ``(seed, stream id,
+block)`` for consecutive blocks of 2^24 elements, so two layouts that share a
+tensor shape (for example the V cache of the asymmetric layout and of its
+symmetric twin) receive identical bytes, and a tensor of another shape (K, Q)
+is drawn from the same streams at its own size.  Blocks are filled by a pool
+of threads; the values do not depend on how many.
 
 bf16 tensors are returned as their raw ``uint16`` bit patterns, obtained from
 float32 normals by round-to-nearest-even; :func:`bf16_bits_to_f32` widens them
@@ -17,6 +19,8 @@ back exactly.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -26,11 +30,13 @@ S_Q, S_K, S_V, S_KNEW, S_VNEW, S_LEN, S_OUTLIER = 1, 2, 3, 4, 5, 6, 7
 S_H, S_WGATE, S_WUP, S_WDOWN = 8, 9, 10, 11
 
 BF16_NAN = np.uint16(0x7FC0)
-_BLOCK = 1 << 24  # elements generated per block, bounds host memory
+_BLOCK = 1 << 24  # elements per generator block (part of the values' definition)
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
-def _rng(seed: int, stream: int) -> np.random.Generator:
-    return np.random.default_rng([int(seed), int(stream)])
+def _rng(seed: int, stream: int, block: int | None = None) -> np.random.Generator:
+    key = [int(seed), int(stream)] if block is None else [int(seed), int(stream), int(block)]
+    return np.random.default_rng(key)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -53,21 +59,32 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 def normal(seed: int, stream: int, shape, dtype: str) -> np.ndarray:
     """N(0,1) samples of ``shape``: float32 array, or uint16 bf16 bits.
 
-    Samples are generated in blocks from one generator, so the values do not
-    depend on the block size and host memory stays bounded for large caches.
+    Element e belongs to block e // 2^24, whose samples come from the
+    generator keyed (seed, stream, block); blocks are filled in parallel
+    (numpy's generators and array arithmetic release the interpreter lock),
+    so the values depend on the seed, the stream and the shape only.
     """
     n = int(np.prod(shape)) if len(shape) else 1
-    g = _rng(seed, stream)
     if dtype == "f32":
         out = np.empty(n, dtype=np.float32)
     elif dtype == "bf16":
         out = np.empty(n, dtype=np.uint16)
     else:
         raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
-    for s in range(0, n, _BLOCK):
+
+    def fill(blk: int) -> None:
+        s = blk * _BLOCK
         e = min(n, s + _BLOCK)
-        x = g.standard_normal(e - s, dtype=np.float32)
+        x = _rng(seed, stream, blk).standard_normal(e - s, dtype=np.float32)
         out[s:e] = x if dtype == "f32" else f32_to_bf16_bits(x)
+
+    n_blocks = -(-n // _BLOCK)
+    if n_blocks <= 1:
+        for blk in range(n_blocks):
+            fill(blk)
+    else:
+        with ThreadPoolExecutor(max_workers=min(_THREADS, n_blocks)) as ex:
+            list(ex.map(fill, range(n_blocks)))
     return out.reshape(shape)
 
 

@@ -55,9 +55,27 @@ def normwise_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.abs(got - ref).max() / scale)
 
 
+def elementwise_stats(got: np.ndarray, ref: np.ndarray) -> dict:
+    """Element-wise error figures reported beside the normwise one: the
+    largest and mean absolute error, and the largest relative error over the
+    elements whose reference is at least a tenth of the largest (relative
+    error is ill-posed for elements near zero)."""
+    d = np.abs(got - ref)
+    a = np.abs(ref)
+    big = a >= 0.1 * a.max() if a.size else a
+    rel = float((d[big] / a[big]).max()) if a.size and big.any() else 0.0
+    return {"max_abs": float(d.max()) if d.size else 0.0,
+            "mean_abs": float(d.mean()) if d.size else 0.0,
+            "max_rel_big": rel}
+
+
 def assert_close(got, ref, dtype, what=""):
     assert not np.isnan(got).any(), f"{what}: NaN in GPU output"
     err = normwise_err(got, ref)
+    st = elementwise_stats(got, ref)
+    print(f"[err] {what}: normwise {err:.3e}, max abs {st['max_abs']:.3e}, "
+          f"mean abs {st['mean_abs']:.3e}, max rel (|ref| >= max/10) {st['max_rel_big']:.3e}",
+          flush=True)
     assert err <= TOL[dtype], f"{what}: normwise rel err {err:.3e} > {TOL[dtype]:.0e}"
     return err
 

@@ -78,8 +78,12 @@ def test_decode_rejects_unsupported_and_bad_sizes(lib):
     assert _decode(lib, dtype=0, d_k=256) == UNSUP
     assert _decode(lib, max_ctx=2048, l_cap=1024) == SHAPE
     assert _decode(lib, B=-1) == SHAPE
-    assert _decode(lib, scale=0.0) == SHAPE
+    assert _decode(lib, scale=-0.125) == SHAPE
     assert _decode(lib, scale=float("nan")) == SHAPE
+    assert _decode(lib, scale=float("inf")) == SHAPE
+    # 0 selects the library's default 1/sqrt(d_k): validation goes on to the
+    # next check (here the workspace size).
+    assert _decode(lib, scale=0.0, ws_bytes=0) == WS
     assert _decode(lib, chunk=100) == SHAPE   # not a multiple of 64
     assert _decode(lib, chunk=-64) == SHAPE
 
@@ -259,7 +263,7 @@ def test_paged_and_compat_validation(lib):
     assert pre(P=96) == SHAPE and pre(N=0) == SHAPE and pre(MB=0) == SHAPE
     assert pre(tab=None) == NULL and pre(q=None) == NULL
     assert pre(vp=FAKE + 8) == ALIGN and pre(dtype=0) == UNSUP and pre(d_k=32) == UNSUP
-    assert pre(scale=0.0) == SHAPE and pre(T=0) == OK and pre(B=0, tab=None) == OK
+    assert pre(scale=-1.0) == SHAPE and pre(T=0) == OK and pre(B=0, tab=None) == OK
 
     def sel(**kw):
         a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=1, P=64, N=16, MB=16,

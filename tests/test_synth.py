@@ -25,14 +25,20 @@ def test_bf16_roundtrip_is_exact_on_representable_values():
     np.testing.assert_array_equal(synth.f32_to_bf16_bits(f[finite]), bits[finite])
 
 
-def test_normal_is_deterministic_and_block_independent(monkeypatch):
+def test_normal_is_deterministic_and_thread_count_independent(monkeypatch):
+    monkeypatch.setattr(synth, "_BLOCK", 257)          # many blocks
     a = synth.normal(5, synth.S_K, (3, 1000), "f32")
-    monkeypatch.setattr(synth, "_BLOCK", 257)
+    monkeypatch.setattr(synth, "_THREADS", 1)
     b = synth.normal(5, synth.S_K, (3, 1000), "f32")
     np.testing.assert_array_equal(a, b)
     c = synth.normal(6, synth.S_K, (3, 1000), "f32")
     assert not np.array_equal(a, c)
     assert abs(a.mean()) < 0.1 and abs(a.std() - 1) < 0.1
+    # Blocks are distinct streams: no two blocks repeat each other.
+    assert not np.array_equal(a.reshape(-1)[:257], a.reshape(-1)[257:514])
+    # bf16 bits are the rounding of the same float32 samples.
+    d = synth.normal(5, synth.S_K, (3, 1000), "bf16")
+    np.testing.assert_array_equal(d, synth.f32_to_bf16_bits(a))
 
 
 def test_symmetric_twin_shares_value_bytes():
