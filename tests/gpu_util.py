@@ -9,6 +9,19 @@ import synth
 # Tolerances: max normwise relative error max|gpu - ref| / max|ref| per output
 # tensor, for fp32 inputs and for bf16 inputs with fp32 accumulation.
 TOL = {"f32": 1e-5, "bf16": 2e-2}
+# Regression bounds, well inside the contract, so that a kernel that loses a
+# few bits fails a test even while it still meets TOL:
+#  bf16: 4 * 2^-9.  One 2^-9 is the bf16 rounding of each output element
+#  (round to nearest even: relative error <= 2^-9, so <= 2^-9 of the largest
+#  element); up to three more cover the bf16 rounding of the weights that
+#  enter fp32-accumulated products (the decode's probabilities, the prefill's
+#  P tile, augmented Q's gated intermediate), each term off by <= 2^-9
+#  relative, whose effect on an element grows where the weighted sum
+#  cancels.  Measured: at most 4.7e-3 (the 70-row 32/4/16 prefill).
+#  f32: 32 * 2^-24, for the hardware base-2 exponential (about one unit in
+#  the last place), the rounding of scores of magnitude up to ~10 and the
+#  fp32 accumulation.  Measured: at most 6.2e-7.
+REGRESS_TOL = {"f32": 32 * 2.0 ** -24, "bf16": 4 * 2.0 ** -9}
 # lse is an fp32 log-sum-exp of scores computed exactly from the inputs; its
 # absolute error is bounded by fp32 rounding of scores of size ~|s|.
 LSE_TOL = {"f32": 2e-5, "bf16": 2e-4}
@@ -77,6 +90,9 @@ def assert_close(got, ref, dtype, what=""):
           f"mean abs {st['mean_abs']:.3e}, max rel (|ref| >= max/10) {st['max_rel_big']:.3e}",
           flush=True)
     assert err <= TOL[dtype], f"{what}: normwise rel err {err:.3e} > {TOL[dtype]:.0e}"
+    assert err <= REGRESS_TOL[dtype], (
+        f"{what}: normwise rel err {err:.3e} meets the {TOL[dtype]:.0e} contract but exceeds "
+        f"the regression bound {REGRESS_TOL[dtype]:.2e}")
     return err
 
 
