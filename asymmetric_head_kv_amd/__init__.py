@@ -47,6 +47,7 @@ SIGNATURES = {
     "diffqkv_prefill_paged": (_i32, [_i32] * 11 + [_f32] + [_vp] * 8 + [_sz, _vp]),
     "diffqkv_decode_split": (_i32, [_i32] * 9 + [_f32] + [_vp] * 6 + [_i32, _vp, _sz, _vp]),
     "diffqkv_decode_append": (_i32, [_i32] * 9 + [_f32] + [_vp] * 8 + [_i32, _vp, _sz, _vp]),
+    "diffqkv_decode_append_noalloc": (_i32, [_i32] * 9 + [_f32] + [_vp] * 8 + [_i32, _vp]),
     "diffqkv_decode_combine": (_i32, [_i32] * 9 + [_vp] * 3 + [_i32, _vp, _sz, _vp]),
     "diffqkv_decode_selective_workspace": (_i32, [_i32] * 8 + [ctypes.POINTER(_sz)]),
     "diffqkv_decode_selective": (_i32, [_i32] * 9 + [_f32, _i32] + [_vp] * 10 + [_sz, _vp]),

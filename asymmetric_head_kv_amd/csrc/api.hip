@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "diffqkv.h"
 #include "launch.h"
 
@@ -183,6 +185,43 @@ int selective_layout(int n_q, int n_k, int batch, int max_ctx, int top_k, SelLay
 
 }  // namespace
 
+// ------------------------------------------------- static decode scratch
+//
+// diffqkv_decode_append_noalloc keeps the split kernel's partial results in
+// this file-scope device array instead of a caller workspace.  Each GPU the
+// library runs on holds its own copy (kScratchBytes, from module load until
+// the process ends).  In host code `scratch` names a host-side stand-in, not
+// device memory: the device address comes from hipGetSymbolAddress, once
+// per device with that device current, and only that address is passed to
+// kernels.
+namespace {
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of scratch, per device
+
+// The current device's scratch address (looked up on the first call on that
+// device).  Returns DQKV_OK or DQKV_ERR_HIP.
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DQKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return DQKV_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DQKV_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* dqkv_status_str(int32_t status) {
@@ -249,6 +288,16 @@ int32_t kv_append(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_
   return to_status(dqkv::launch_kv_append(a));
 }
 
+// Points the descriptor's partial-result arrays into a decode workspace:
+// (m, l) pairs first, then the weighted V sums from the next 256-byte
+// boundary.
+static void bind_decode_workspace(dqkv::DecodeArgs* a, void* workspace) {
+  const size_t parts = (size_t)a->batch * a->n_q * a->C;
+  a->part_ml = (float*)workspace;
+  a->part_acc = workspace ? (float*)((char*)workspace + align256(parts * 2 * sizeof(float)))
+                          : nullptr;
+}
+
 // Validates a decode call and fills the launch descriptor.  need_qkv /
 // need_out select which buffers the caller's entry point uses.
 static int prepare_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, int32_t d_v,
@@ -257,7 +306,8 @@ static int prepare_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, in
                           const void* v_cache, const int32_t* ctx_len, void* out,
                           float* lse, int32_t chunk_tokens, void* workspace,
                           size_t workspace_bytes_given, void* stream, bool need_qkv,
-                          bool need_out, dqkv::DecodeArgs* a, bool paged = false) {
+                          bool need_out, dqkv::DecodeArgs* a, bool paged = false,
+                          bool check_ws_ptr = true) {
   int st = check_heads(n_q, n_k, n_v, d_k, d_v);
   if (st) return st;
   st = check_dtype_dims(dtype, d_k, d_v);
@@ -267,9 +317,9 @@ static int prepare_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, in
   if (need_qkv && !resolve_scale(scale, d_k, &scale)) return DQKV_ERR_SHAPE;
   if (need_qkv && (!q || !k_cache || !v_cache)) return DQKV_ERR_NULL;
   if (need_out && !out) return DQKV_ERR_NULL;
-  if (!ctx_len || !workspace) return DQKV_ERR_NULL;
+  if (!ctx_len || (check_ws_ptr && !workspace)) return DQKV_ERR_NULL;
   if ((need_qkv && (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))) ||
-      (need_out && !aligned16(out)) || !aligned16(workspace))
+      (need_out && !aligned16(out)) || (check_ws_ptr && !aligned16(workspace)))
     return DQKV_ERR_ALIGN;
   int S = 0;
   st = resolve_chunk(n_q, n_k, n_v, batch, max_ctx, chunk_tokens, &S, paged);
@@ -286,9 +336,7 @@ static int prepare_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, in
   a->q = q; a->k_cache = k_cache; a->v_cache = v_cache; a->ctx_len = ctx_len;
   a->out = out; a->lse = lse;
   a->k_new = nullptr; a->v_new = nullptr;
-  const size_t parts = (size_t)batch * n_q * C;
-  a->part_ml = (float*)workspace;
-  a->part_acc = (float*)((char*)workspace + align256(parts * 2 * sizeof(float)));
+  bind_decode_workspace(a, workspace);
   a->stream = (hipStream_t)stream;
   return DQKV_OK;
 }
@@ -353,6 +401,37 @@ int32_t diffqkv_decode_append(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k
   if (st) return st;
   if (!k_new || !v_new) return DQKV_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new)) return DQKV_ERR_ALIGN;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  st = to_status(dqkv::launch_decode_split(a));
+  if (st) return st;
+  return to_status(dqkv::launch_decode_combine(a));
+}
+
+int32_t diffqkv_decode_append_noalloc(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                                      int32_t d_v, int32_t dtype, int32_t batch,
+                                      int32_t l_cap, int32_t max_ctx, float scale,
+                                      const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache, const int32_t* ctx_len,
+                                      void* out, float* lse, int32_t chunk_tokens,
+                                      void* stream) {
+  if (batch == 0 && n_q > 0) {
+    int st = check_heads(n_q, n_k, n_v, d_k, d_v);
+    return st ? st : check_dtype_dims(dtype, d_k, d_v);
+  }
+  if ((k_new == nullptr) != (v_new == nullptr)) return DQKV_ERR_NULL;
+  // Host-side checks first; the size check rejects calls whose partials do
+  // not fit the static scratch (DQKV_ERR_WORKSPACE).
+  dqkv::DecodeArgs a;
+  int st = prepare_decode(n_q, n_k, n_v, d_k, d_v, dtype, batch, l_cap, max_ctx, scale, q,
+                          k_cache, v_cache, ctx_len, out, lse, chunk_tokens, nullptr,
+                          kScratchBytes, stream, true, true, &a, false, false);
+  if (st) return st;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return DQKV_ERR_ALIGN;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st) return st;
+  bind_decode_workspace(&a, ws);
   a.k_new = k_new;
   a.v_new = v_new;
   st = to_status(dqkv::launch_decode_split(a));

@@ -161,6 +161,31 @@ int32_t diffqkv_decode_append(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k
                               size_t workspace_bytes, void* stream);
 
 /*
+ * diffqkv_decode_append_noalloc -- diffqkv_decode_append (k_new / v_new may
+ * also both be NULL: then diffqkv_decode) without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The split
+ * kernel's partial results go to a static device array of the library
+ * (16 MiB, one per GPU, held from the first use until the process ends);
+ * the call allocates nothing and frees nothing.  Sizes whose partials need
+ * more than 16 MiB (diffqkv_decode_workspace bytes) return
+ * DQKV_ERR_WORKSPACE.  The array of the CURRENT device is used, so the
+ * stream must belong to the current device.  Every call on a GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (on different
+ * streams) race and must not be issued; calls in order on one stream are
+ * fine (no contents need to survive between calls).  Same result, bit for
+ * bit, as diffqkv_decode_append (or diffqkv_decode) with the same
+ * chunk_tokens.
+ */
+int32_t diffqkv_decode_append_noalloc(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
+                                      int32_t d_v, int32_t dtype, int32_t batch,
+                                      int32_t l_cap, int32_t max_ctx, float scale,
+                                      const void* q, const void* k_new,
+                                      const void* v_new, void* k_cache, void* v_cache,
+                                      const int32_t* ctx_len, void* out, float* lse,
+                                      int32_t chunk_tokens, void* stream);
+
+/*
  * diffqkv_decode_split / diffqkv_decode_combine -- the two halves of
  * diffqkv_decode (or, with k_new / v_new non-NULL, of diffqkv_decode_append),
  * for callers that time or schedule them separately: the pages measure the

@@ -312,3 +312,28 @@ def test_augq_validation(lib):
     assert lib.augq_pack(32, 64, None, FAKE, None) == NULL
     assert lib.augq_pack(32, 64, FAKE, FAKE + 8, None) == ALIGN
     assert lib.augq_pack(0, 64, None, None, None) == OK
+
+
+def test_decode_noalloc_validation(lib):
+    # Host-side checks run before the library looks up its static scratch,
+    # so none of these touches a device.
+    def call(**kw):
+        a = dict(n_q=16, n_k=4, n_v=16, d_k=64, d_v=128, dtype=1, B=1, l_cap=1024,
+                 max_ctx=1024, scale=0.0, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE,
+                 ctx=FAKE, out=FAKE, lse=None, chunk=0)
+        a.update(kw)
+        return lib.diffqkv_decode_append_noalloc(
+            a["n_q"], a["n_k"], a["n_v"], a["d_k"], a["d_v"], a["dtype"], a["B"], a["l_cap"],
+            a["max_ctx"], a["scale"], a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["ctx"],
+            a["out"], a["lse"], a["chunk"], None)
+    assert call(n_k=3) == SHAPE
+    assert call(d_k=48) == UNSUP
+    assert call(kn=None) == NULL          # k_new and v_new: both or neither
+    assert call(q=None, kn=None, vn=None) == NULL
+    assert call(vn=FAKE + 8) == ALIGN
+    assert call(scale=-1.0) == SHAPE
+    assert call(B=0) == OK
+    # Partials beyond the 16 MiB static scratch: 16 sequences x 16 heads x
+    # 8192 chunks of 64 rows need far more.
+    assert call(B=16, l_cap=8192 * 64, max_ctx=8192 * 64, chunk=64) == WS
+
