@@ -26,7 +26,9 @@ __all__ = ["DQKVError", "lib_path", "load", "decode", "decode_chunk",
            "prefill", "prefill_paged", "prefill_workspace_bytes", "kv_append", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_HERE, "libdiffqkv.so")
+# The in-tree library; DQKV_LIBRARY names another build of the same sources
+# (the test-suite's sanitizer build of the host code).
+lib_path = os.environ.get("DQKV_LIBRARY") or os.path.join(_HERE, "libdiffqkv.so")
 
 STATUS = {0: "DQKV_OK", -1: "DQKV_ERR_NULL", -2: "DQKV_ERR_SHAPE",
           -3: "DQKV_ERR_UNSUPPORTED", -4: "DQKV_ERR_WORKSPACE",
