@@ -442,6 +442,8 @@ def decode_record(name: str, steps: int, warmup: int, chunk: int = 0) -> dict:
            "split_us": round(split_ms * 1e3, 2), "combine_us": round(comb_ms * 1e3, 2),
            "split_GBps": round(split_gbs, 1),
            "split_frac_of_hbm_peak": round(split_gbs / HBM_PEAK_GBS, 4),
+           "split_alg_bytes_per_launch": bn.alg_bytes_split,
+           "split_traffic": pmc_traffic(name),
            "dtype": bn.case.dtype,
            "shape": {"batch": bn.B, "max_ctx": bn.max_ctx, "ctx_sum": int(bn.ctx.sum()),
                      "n_q": n_q, "n_k": n_k, "n_v": n_v, "d_k": d_k, "d_v": d_v},
