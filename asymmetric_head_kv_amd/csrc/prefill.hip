@@ -19,11 +19,13 @@
 // transposed so that each lane owns one query row:
 //   S^T[key][q]  = K . Q^T   (v_mfma_f32_32x32x16_bf16: A = K from LDS,
 //                             B = Q^T held in registers for the whole walk)
-//   P^T          = 2^(S^T * scale * log2 e - m), online max / sum per lane
-//                  (the sum over the bf16-rounded weights, v_dot2_f32_bf16),
-//                  the two lane halves of a query row joined by one shuffle;
-//                  the running max m is moved (and O rescaled) only when it
-//                  grows by more than 2^8 (exact: O and l share the stale m)
+//   P^T          = 2^(S^T * scale * log2 e - m), row sums per lane (over
+//                  the bf16-rounded weights, v_dot2_f32_bf16), the two lane
+//                  halves of a query row joined by one v_permlane32_swap;
+//                  m is the row max of the split's first key tile and is
+//                  then kept, so later weights may exceed 1; a 32-key block
+//                  whose weights pass 2^64 moves m to that block's max
+//                  first (exact: O and l always share one m)
 //   O^T[d][q]   += V^T . P^T (A = V^T from LDS, B = P^T straight from the
 //                             S^T accumulators, rounded to bf16)
 // In the 32x32 accumulator layout lane l holds column l % 32 and rows
@@ -75,6 +77,25 @@ struct PfLds {
   __device__ static int kswz(int j) { return (j / KR256) & (K16 - 1); }
   __device__ static int vswz(int j) { return 4 * ((j / VR256) & (V16 / 4 - 1)); }
 };
+
+// The two lane halves of a query row joined: v_permlane32_swap hands lanes
+// 0-31 the upper half's values and lanes 32-63 the lower half's.
+// (Issued as inline asm: through the builtin the compiler has dropped the
+// second result and returned the first one twice.  The s_nop gives the two
+// wait states a swap needs after a VALU write of its operands.)
+__device__ __forceinline__ f32x2 halves(float v) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return f32x2{a, b};
+}
+__device__ __forceinline__ float halves_max(float v) {
+  const f32x2 h = halves(v);
+  return fmaxf(h[0], h[1]);
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const f32x2 h = halves(v);
+  return h[0] + h[1];
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
@@ -282,17 +303,33 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
       for (int r = 0; r < 16; r += 2) smax = fmaxf(fmaxf(smax, sx[kb][r]), sx[kb][r + 1]);
     }
-    smax = fmaxf(smax, __shfl_xor(smax, 32));
+    smax = halves_max(smax);
     return smax * qscale;
   };
-  // Lazy rescaling: the running max only moves (and O, l are rescaled) when
-  // some row's max grows by more than 2^8; otherwise the stale max is kept,
-  // probabilities stay <= 256, and O / l is unchanged.
-  auto rescale = [&](float m_tile) {
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.f) != 0) {
-      const float m_new = fmaxf(m_run, m_tile);
+  // Row maximum of one 32-key block of the scaled scores.
+  auto block_max = [&](const f32x16 (&sx)[2], int kb) -> float {
+    float smax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) smax = fmaxf(fmaxf(smax, sx[kb][r]), sx[kb][r + 1]);
+    return halves_max(smax) * qscale;
+  };
+  // Overflow guard: the running max m_run is taken from the split's first
+  // tile and then kept; later tiles' weights 2^(s - m_run) may exceed 1.  A
+  // block whose weights pass 2^64 (inf included) is caught through its row
+  // sums before its P.V product; the running max then moves to the tile's
+  // true max, O, l and the tile's earlier row sums are rescaled, and the
+  // block's weights are recomputed.
+  constexpr float kPLimit = 18446744073709551616.f;  // 2^64
+  auto overflowed = [&](const float (&ps)[2]) {
+    return __builtin_amdgcn_ballot_w64(!(ps[0] + ps[1] <= kPLimit)) != 0;
+  };
+  auto rescale_to = [&](float m_tile, float (&ps_prev)[2]) {
+    const float m_new = fmaxf(m_run, m_tile);
+    if (m_new > m_run) {
       const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
+      ps_prev[0] *= alpha;
+      ps_prev[1] *= alpha;
 #pragma unroll
       for (int n = 0; n < NB; ++n) o[n] *= alpha;
       m_run = m_new;
@@ -316,6 +353,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   // P for one 32-key block: exponentials, row sums, bf16 operands.
   auto make_p = [&](const f32x16 (&sx)[2], int kb, bf16x8 (&pb)[4], float (&psum)[2],
                     float m_use) {
+    psum[0] = 0.f;
+    psum[1] = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float p0 = fast_exp2(fmaf(sx[kb][r], qscale, -m_use));
@@ -351,12 +390,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   // independent VALU work of the same wave:
   //   A: S^T(t + 1) = K(t + 1) Q^T      with  P(t) for keys 0-31
   //   B: O^T += V^T(t) P^T, keys 0-31   with  P(t) for keys 32-63
-  //   C: O^T += V^T(t) P^T, keys 32-63  with  the row max of S^T(t + 1)
+  //   C: O^T += V^T(t) P^T, keys 32-63  with  the causal mask of S^T(t + 1)
   // LDS stage s holds K of tiles t_begin + s, + s + 2, ... and V of the same
   // tiles, each loaded one iteration apart.  (On the last iteration phase A
   // multiplies a stale K stage; its result is never used.)
   f32x16 sa0[2], sa1[2];
-  float m_tile = -INFINITY;
   if (t_begin < t_end) {
     issue_k(t_begin, 0);
     issue_v(t_begin, 0);
@@ -365,38 +403,51 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     __syncthreads();
     qk(stage_k(0), sa0);
     mask(sa0, t_begin);
-    m_tile = tile_max(sa0);
+    m_run = tile_max(sa0);
   }
-  auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], int t) {
-    const int i = t - t_begin;
-    const int cur = i & 1, nxt = cur ^ 1;
+  auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], int t, const int cur) {
+    const int nxt = cur ^ 1;
     // K(t + 1) and V(t) have landed for every wave; every wave is done with
     // K(t) and V(t - 1), whose places receive K(t + 2) and V(t + 1).
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t + 2 < t_end) issue_k(t + 2, cur);
     if (t + 1 < t_end) issue_v(t + 1, nxt);
-    rescale(m_tile);
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;  // rows with nothing visible yet
-    float psum[2] = {0.f, 0.f};  // two chains of row-sum additions
+    float m_use = m_run == -INFINITY ? 0.f : m_run;  // rows with nothing visible
+    float psA[2], psB[2];  // row sums of keys 0-31 and 32-63, two chains each
     bf16x8 pb[4];
     // The three phases run at raised wave priority (back to normal before
     // the next tile's wait): measured 2.5% faster than without.
     __builtin_amdgcn_s_setprio(1);
     bf16x8 ka[2 * KS];
-    kread(stage_k(nxt), ka);
-    __builtin_amdgcn_sched_barrier(0);  // the K reads go out first
+    {
+      const unsigned char* kl = stage_k(nxt);
+#pragma unroll
+      for (int u = 0; u < KS; ++u)
+        ka[u] = as_bf16x8(*reinterpret_cast<const u32x4*>(kl + k_rd[u]));
+      __builtin_amdgcn_sched_barrier(0);  // the first key block's reads go out first
+#pragma unroll
+      for (int u = KS; u < 2 * KS; ++u)
+        ka[u] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            kl + 32 * Lds::K16 * 16 + k_rd[u - KS]));
+    }
     qk2(ka, sn);
-    make_p(sc, 0, pb, psum, m_use);
+    make_p(sc, 0, pb, psA, m_use);
 #pragma unroll
     for (int k = 0; k < 2 * KS; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read for a later MFMA
     }
+    if (overflowed(psA)) {
+      float none[2] = {0.f, 0.f};
+      rescale_to(block_max(sc, 0), none);
+      m_use = m_run == -INFINITY ? 0.f : m_run;
+      make_p(sc, 0, pb, psA, m_use);
+    }
     pv(stage_v(cur), 0, pb);
     pv(stage_v(cur), 1, pb);
-    make_p(sc, 1, pb, psum, m_use);
+    make_p(sc, 1, pb, psB, m_use);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
@@ -404,13 +455,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads for a later MFMA
     }
-    float ps = psum[0] + psum[1];
-    ps += __shfl_xor(ps, 32);
+    if (overflowed(psB)) {
+      rescale_to(block_max(sc, 1), psA);
+      m_use = m_run == -INFINITY ? 0.f : m_run;
+      make_p(sc, 1, pb, psB, m_use);
+    }
+    const float ps = halves_sum((psA[0] + psA[1]) + (psB[0] + psB[1]));
     l_run += ps;
     mask(sn, t + 1);
     pv(stage_v(cur), 2, pb);
     pv(stage_v(cur), 3, pb);
-    m_tile = tile_max(sn);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
@@ -422,10 +476,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   };
   int t = t_begin;
   for (; t + 1 < t_end; t += 2) {
-    step(sa0, sa1, t);
-    step(sa1, sa0, t + 1);
+    step(sa0, sa1, t, 0);
+    step(sa1, sa0, t + 1, 1);
   }
-  if (t < t_end) step(sa0, sa1, t);
+  if (t < t_end) step(sa0, sa1, t, 0);
 
   // Store this lane's query row: rows 8*(r/4)+4h+r%4 of each 32-column block
   // of O^T are value columns.  One split: normalise and write bf16 out / lse.

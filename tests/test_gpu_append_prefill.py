@@ -130,6 +130,30 @@ def test_prefill_rows_without_visible_keys():
     assert_lse_close(lse[0, 30:], ref_lse[0, 30:], "bf16", "rows with keys")
 
 
+@pytest.mark.parametrize("with_lse", [True, False], ids=["lse", "no-lse"])
+def test_prefill_logits_far_above_the_first_tile(with_lse):
+    # The kernel keeps each row's max from the first key tile of its split;
+    # keys whose scaled logits lie ~100 and ~190 (log2 units) above it make
+    # the later weights overflow 2^64 and fp32, which its guard must catch.
+    # q = 1 everywhere; two cache rows per K head are set to 9.0 and 17.0.
+    case = synth.make_case(204, dtype="bf16", batch=1, n_q=16, n_k=4, n_v=16, d_k=64, d_v=128,
+                           ctx_len=[1500], l_cap=1536, t_new=600, poison_tail=True)
+    case.q[...] = 0x3F80                      # bf16 1.0
+    case.k_cache[:, :, 1000, :] = 0x4110      # bf16 9.0: 2^104 above a typical row max
+    case.k_cache[:, :, 1300, :] = 0x4188      # bf16 17.0: 2^196, past fp32's range
+    q, k, v = case.widened()
+    rows = [(0, r) for r in range(0, 600, 7)] + [(0, 599)]
+    ref, ref_lse = oracle.prefill(q, k, v, case.ctx_len, case.scale, rows=rows)
+    _say("prefill logits far above the first tile", "lse" if with_lse else "no lse")
+    for split in (True, False):
+        got, lse = run_prefill(case, with_lse, split)
+        idx = [r for _, r in rows]
+        assert np.isfinite(got).all()
+        assert_close(got[0, idx], ref[0, idx], "bf16", f"spiked logits split={split}")
+        if with_lse:
+            assert_lse_close(lse[0, idx], ref_lse[0, idx], "bf16", f"spiked logits split={split}")
+
+
 def test_prefill_full_workload_every_row():
     # The benchmark's prefill (2048 new rows on 30720 cached, 16 query heads,
     # key splits as the benchmark runs it), every one of the 2048 x 16 rows
