@@ -610,6 +610,27 @@ def hbm_copy_gbs(nbytes: int = 2 << 30, reps: int = 10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def bf16_gemm_tflops(n: int = 8192, reps: int = 20):
+    """Practical dense-matrix-core rate on this machine: torch's bf16 GEMM
+    (hipBLASLt) on n x n x n with every CU busy, for comparison with the
+    prefill's own rate (both run under the same board power limit)."""
+    import torch
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    c = a @ b
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del a, b, c
+    torch.cuda.empty_cache()
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
 def _cpu_threads() -> int:
     """Worker threads for the oracle: the host's CPUs, at most 16 (one GPU's
     share of a host)."""
@@ -829,6 +850,9 @@ def main():
         if not args.no_prefill:
             log("prefill 2048 on 30720")
             result["prefill"] = prefill_bench()
+            g = bf16_gemm_tflops()
+            result["prefill"]["bf16_gemm_8192_tflops"] = round(g, 1)
+            result["prefill"]["frac_of_gemm"] = round(result["prefill"]["tflops"] / g, 4)
         if not args.no_augq:
             log("augmented Q")
             result["augq"] = augq_bench()
