@@ -97,14 +97,18 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total)
 }
 
 struct Threshold {
-  uint32_t key;  // the k-th largest key
-  int need_eq;   // rows with this key to take (the lowest-indexed ones)
+  uint32_t key;  // keys above it are taken (the k-th largest key, or one below a whole bin)
+  int need_eq;   // rows with this key to take as well (the lowest-indexed ones)
 };
 
 // k-th largest of the n keys key(0..n-1), 1 <= k <= n, by radix select from
 // the most significant digit.  Invariant before each pass: the keys that
 // match the digits fixed so far number at least krem, and the keys above
-// that prefix number k - krem.  hist: kBins LDS words; red: 8 LDS ints.
+// that prefix number k - krem.  A pass whose chosen bin holds exactly krem
+// keys ends the search: every key with that prefix is taken, so the
+// threshold is the prefix's lowest key minus one with no equal keys taken
+// (the same set as the remaining passes would give).  hist: kBins LDS
+// words; red: 8 LDS ints.
 template <class KeyF>
 __device__ Threshold block_select_threshold(KeyF key, int n, int k, uint32_t* hist, int* red) {
   const int tid = threadIdx.x;
@@ -140,6 +144,7 @@ __device__ Threshold block_select_threshold(KeyF key, int n, int k, uint32_t* hi
         if (run + cnt[e] >= krem) {
           red[4] = kBins - 1 - BPT * tid - e;
           red[5] = krem - run;
+          red[6] = cnt[e] == krem - run;
           break;
         }
         run += cnt[e];
@@ -150,8 +155,12 @@ __device__ Threshold block_select_threshold(KeyF key, int n, int k, uint32_t* hi
     krem = red[5];
     prefix |= digit << shift;
     pmask |= dmask << shift;
+    if (red[6] != 0 && prefix != 0u) {  // the whole bin is taken
+      __syncthreads();  // red[4..6] are rewritten by the next caller
+      return Threshold{prefix - 1u, 0};
+    }
   }
-  __syncthreads();  // red[4], red[5] are rewritten by the next caller
+  __syncthreads();  // red[4..6] are rewritten by the next caller
   return Threshold{prefix, krem};
 }
 
@@ -209,7 +218,7 @@ __device__ __forceinline__ int reg_index(int e) {
 }
 
 // hist: three kBins-word histograms (one per digit pass), zeroed and made
-// visible by a barrier before the call.
+// visible by a barrier before the call.  Ends early as the block variant.
 template <int E>
 __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k,
                                           uint32_t* hist, int* red) {
@@ -242,6 +251,7 @@ __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k
         if (run + cnt[e] >= krem) {
           red[4] = kBins - 1 - BPT * tid - e;
           red[5] = krem - run;
+          red[6] = cnt[e] == krem - run;
           break;
         }
         run += cnt[e];
@@ -251,6 +261,10 @@ __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k
     prefix |= (uint32_t)red[4] << shift;
     pmask |= dmask << shift;
     krem = red[5];
+    if (red[6] != 0 && prefix != 0u) {  // the whole bin is taken (as above)
+      __syncthreads();
+      return Threshold{prefix - 1u, 0};
+    }
   }
   __syncthreads();
   return Threshold{prefix, krem};
