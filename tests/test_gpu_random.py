@@ -2,7 +2,10 @@
 head layouts (either side the smaller one), head dimensions, dtypes, batch
 sizes, ragged lengths (1 row .. several chunks, ragged tails) and chunk
 lengths; selective V with random top_k; the paged cache with random page
-sizes.  Every configuration is printed before it runs."""
+sizes; the causal prefill over random head layouts, head dimensions, new-row
+counts (rows with no visible key included), scales, key splits, paged
+caches and planted logits far above the first key tile's.  Every
+configuration is printed before it runs."""
 
 import sys
 
@@ -158,3 +161,84 @@ def test_decode_large_ragged_batch(seed):
     err = assert_close(to_host(out), ref, dtype, f"seed {seed}")
     assert_lse_close(to_host(lse), ref_lse, dtype, f"seed {seed}")
     _say(f"  normwise rel err {err:.2e}")
+
+
+def _pages_of(case, P, rng):
+    """The case's cache rows in pages of P rows, in a seeded random page
+    order, with one table entry past each sequence's last page set to -1."""
+    B = case.batch
+    lens = [int(x) for x in case.ctx_len]
+    need = [max(1, -(-L // P)) for L in lens]
+    n_pages = sum(need) + 2
+    order = rng.permutation(n_pages)
+    table = np.full((B, max(need) + 1), -1, dtype=np.int32)
+    kp = np.zeros((n_pages,) + case.k_cache.shape[1:2] + (P,) + case.k_cache.shape[3:],
+                  dtype=case.k_cache.dtype)
+    vp = np.zeros((n_pages,) + case.v_cache.shape[1:2] + (P,) + case.v_cache.shape[3:],
+                  dtype=case.v_cache.dtype)
+    nxt = 0
+    for b, L in enumerate(lens):
+        for blk in range(need[b]):
+            page = int(order[nxt])
+            nxt += 1
+            table[b, blk] = page
+            r1 = min((blk + 1) * P, L)
+            if r1 > blk * P:
+                kp[page, :, :r1 - blk * P] = case.k_cache[b, :, blk * P:r1]
+                vp[page, :, :r1 - blk * P] = case.v_cache[b, :, blk * P:r1]
+    return kp, vp, table
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_prefill_random_shapes(seed):
+    rng = np.random.default_rng(3000 + seed)
+    n_q = int(rng.choice([4, 8, 12, 16, 32]))
+    n_k = int(rng.choice(_divisors(n_q)))
+    n_v = int(rng.choice(_divisors(n_q)))
+    d_k = int(rng.choice([64, 128]))
+    d_v = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 4))
+    T = int(rng.integers(1, 330))
+    lens = [int(x) for x in rng.integers(max(1, T // 2), T + 1400, size=B)]
+    cap = max(lens) + int(rng.integers(0, 70))
+    scale = None if rng.random() < 0.5 else float(rng.uniform(0.03, 0.4))
+    spike = rng.random() < 0.4
+    _say("random prefill", seed, (n_q, n_k, n_v, d_k, d_v), "T", T, lens, cap, "scale", scale,
+         "spike", spike)
+    case = synth.make_case(800 + seed, dtype="bf16", batch=B, n_q=n_q, n_k=n_k, n_v=n_v,
+                           d_k=d_k, d_v=d_v, ctx_len=lens, l_cap=cap, t_new=T,
+                           poison_tail=True, scale=scale)
+    if spike:
+        # q = 1 everywhere and, late in each sequence, one key row of 6.0 per
+        # K head: its logit lies far above every first key tile's max.
+        case.q[...] = 0x3F80
+        for b, L in enumerate(lens):
+            j = int(rng.integers(L // 2, L))
+            case.k_cache[b, :, j, :] = 0x40C0
+    qw, kw, vw = case.widened()
+    ref, ref_lse = oracle.prefill_all_rows(qw, kw, vw, case.ctx_len, case.scale)
+    q, k, v, ctx = upload(case)
+    outs = {}
+    for with_lse in (True, False):
+        for split in (True, False):
+            lse = (torch.empty((B, T, n_q), dtype=torch.float32, device="cuda")
+                   if with_lse else None)
+            ws = None if split else torch.empty(0, dtype=torch.uint8, device="cuda")
+            out, lse = dq.prefill(q, k, v, ctx, scale=case.scale, lse=lse, workspace=ws)
+            torch.cuda.synchronize()
+            what = f"seed {seed} lse={with_lse} split={split}"
+            got = to_host(out)
+            assert np.isfinite(got).all(), what
+            assert_close(got, ref, "bf16", what)
+            if with_lse:
+                assert_lse_close(to_host(lse), ref_lse, "bf16", what)
+                outs[split] = (raw_host(out), raw_host(lse))
+    # The same prefill over a paged copy of the cache: bit-identical.
+    P = int(rng.choice([64, 128, 256]))
+    kp, vp, table = _pages_of(case, P, rng)
+    lse_p = torch.empty((B, T, n_q), dtype=torch.float32, device="cuda")
+    out_p, _ = dq.prefill_paged(q, to_dev(kp, "bf16"), to_dev(vp, "bf16"), ints_to_dev(table),
+                                ctx, scale=case.scale, lse=lse_p)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(raw_host(out_p), outs[True][0])
+    np.testing.assert_array_equal(raw_host(lse_p), outs[True][1])
