@@ -71,6 +71,28 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_logits_far_above_the_rest(dtype):
+    # q = 1 everywhere; a few K rows far larger than the rest, in different
+    # chunks: their logits lie ~100 and ~190 (log2 units) above every other
+    # row's, past fp32's exponent range for the second.  Each chunk's running
+    # max and the combine's merge must keep the result finite and exact.
+    case = synth.make_case(611, dtype=dtype, batch=2, n_q=16, n_k=4, n_v=16, d_k=64, d_v=128,
+                           ctx_len=[3000, 1700], l_cap=3072, poison_tail=True)
+    one, nine, seventeen = (0x3F80, 0x4110, 0x4188) if dtype == "bf16" else (1.0, 9.0, 17.0)
+    case.q[...] = one
+    case.k_cache[0, :, 2100, :] = nine
+    case.k_cache[0, :, 2950, :] = seventeen
+    case.k_cache[1, :, 77, :] = seventeen
+    ref, ref_lse = oracle_decode(case)
+    for chunk in (0, 64, 320):
+        _say("decode logits far above the rest", dtype, "chunk", chunk)
+        got, lse = run_decode(case, chunk=chunk)
+        assert np.isfinite(got).all()
+        assert_close(got, ref, dtype, f"spiked decode chunk={chunk}")
+        assert_lse_close(lse, ref_lse, dtype, f"spiked decode chunk={chunk}")
+
+
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-{c[4]}x{c[5]}")
 def test_decode_small_matches_oracle(cfg):
     dtype, n_q, n_k, n_v, d_k, d_v, lens, cap = cfg

@@ -171,6 +171,24 @@ def test_selective_ties_go_to_lower_rows(dtype):
         assert_close(to_host(out)[0, i], ref, dtype, f"ties head {i}")
 
 
+def test_selective_logits_far_above_the_rest():
+    # q = 1; a few K rows far larger than the rest: they must be chosen, and
+    # their weights (full softmax, fp32 logits ~100 and ~190 log2 units above
+    # the others) dominate the output.
+    case = synth.make_case(612, dtype="bf16", batch=2, n_q=16, n_k=4, n_v=16, d_k=64, d_v=128,
+                           ctx_len=[5000, 2100], l_cap=5000, poison_tail=True)
+    case.q[...] = 0x3F80
+    case.k_cache[0, :, 4100, :] = 0x4110
+    case.k_cache[0, :, 17, :] = 0x4188
+    case.k_cache[1, :, 2099, :] = 0x4188
+    _say("selective logits far above the rest")
+    out, lse, sel = run_selective(case, 100)
+    s = sel.cpu().numpy()
+    assert (s[0] == 17).any(axis=1).all() and (s[0] == 4100).any(axis=1).all()
+    assert (s[1] == 2099).any(axis=1).all()
+    check_selective(case, 100, out, lse, sel, "spiked selective")
+
+
 def test_selective_empty_context():
     case = synth.make_case(304, dtype="bf16", batch=2, n_q=8, n_k=2, n_v=8, d_k=64, d_v=128,
                            ctx_len=[0, 300], l_cap=320, poison_tail=True)
