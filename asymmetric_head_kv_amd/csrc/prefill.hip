@@ -315,10 +315,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   };
   // Overflow guard: the running max m_run is taken from the split's first
   // tile and then kept; later tiles' weights 2^(s - m_run) may exceed 1.  A
-  // block whose weights pass 2^64 (inf included) is caught through its row
-  // sums before its P.V product; the running max then moves to the tile's
-  // true max, O, l and the tile's earlier row sums are rescaled, and the
-  // block's weights are recomputed.
+  // 32-key block whose weights pass 2^64 (inf included) is caught through
+  // its row sums before its P.V product; the running max then moves to that
+  // block's own max, O, l and the tile's earlier row sums are rescaled, and
+  // the block's weights are recomputed (no weight then exceeds 1).
   constexpr float kPLimit = 18446744073709551616.f;  // 2^64
   auto overflowed = [&](const float (&ps)[2]) {
     return __builtin_amdgcn_ballot_w64(!(ps[0] + ps[1] <= kPLimit)) != 0;
