@@ -588,6 +588,28 @@ def augq_bench(steps: int = 200):
                         "frac_mfma": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4)}
         log(f"augq M={M}: {us:.2f} us")
         del g
+    # Reference at 2048 tokens: torch's bf16 GEMMs (hipBLASLt) on the same
+    # shapes, gate and up as one n = 2 d_i product, then the down product
+    # (the gating's elementwise step left out), timed on the same box.
+    h = h_all.contiguous()
+    wgu = torch.cat([up(case.w_gate), up(case.w_up)]).t()        # [d_m, 2 d_i]
+    wd = up(case.w_down).t()                                      # [d_i, d_out]
+    a_in = torch.randn(2048, d_i, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        g_ = h @ wgu
+        q_ = a_in @ wd
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(20):
+        torch.matmul(h, wgu, out=g_)
+        torch.matmul(a_in, wd, out=q_)
+    t1.record()
+    torch.cuda.synchronize()
+    ref_us = t0.elapsed_time(t1) / 20 * 1e3
+    out["M2048"]["torch_gemms_us"] = round(ref_us, 2)
+    out["M2048"]["time_over_torch_gemms"] = round(out["M2048"]["us"] / ref_us, 3)
+    log(f"augq M=2048 torch GEMMs: {ref_us:.2f} us")
     return out
 
 
