@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
       for (int r = 0; r < KR; ++r) {
         const int j = min(j0 + k_row(r), n_keys - 1);
-        dma16(kbase + (uint32_t)((j & row_mask) * DK + k_off(r)), (lds_dma_t*)(kl + r * 4096));
+        dma16(kbase + (size_t)(j & row_mask) * DK + k_off(r), (lds_dma_t*)(kl + r * 4096));
       }
     }
   };
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
       for (int r = 0; r < VR; ++r) {
         const int j = min(j0 + v_row(r), n_keys - 1);
-        dma16(vbase + (uint32_t)((j & row_mask) * DV + v_off(r)), (lds_dma_t*)(vl + r * 4096));
+        dma16(vbase + (size_t)(j & row_mask) * DV + v_off(r), (lds_dma_t*)(vl + r * 4096));
       }
     }
   };
