@@ -368,12 +368,14 @@ class DecodeBench:
 
     def time_kernels(self, steps: int):
         """Average duration (ms) of the split kernel and of the combine kernel,
-        each timed alone: a graph of back-to-back launches of that kernel over
-        the cache replicas, replayed between two events on the launch stream."""
+        each timed alone: a graph of back-to-back launches of that kernel
+        (cycling over the cache replicas, at least 16 launches so that a replay
+        outlasts its submission from the host), replayed between two events
+        on the launch stream."""
         torch = self.torch
-        R = self.replicas
+        R = max(16, self.replicas)
         out = []
-        for fn in (self.split, lambda r: self.combine()):
+        for fn in (lambda r: self.split(r % self.replicas), lambda r: self.combine()):
             g = self._graph(fn, R)
             g.replay()
             torch.cuda.synchronize()
