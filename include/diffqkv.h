@@ -399,7 +399,10 @@ int32_t kv_group_sharing(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
  * decode, q [M][d_out] is the query tensor [B][n_q][d_k] that diffqkv_decode
  * takes.  d_m and d_i multiples of 1024, d_out a multiple of 16; h, the
  * packed weights and q 16-byte aligned.  workspace: augq_workspace bytes
- * (M * d_i bf16), 16-byte aligned.  Two kernels on `stream`.
+ * (M * d_i bf16), 16-byte aligned; it receives a, row-major [M][d_i], except
+ * for M <= 16, where it is chunk-major [d_i / 8][M][8] (element (r, c) at
+ * ((c / 8) M + r) 8 + c % 8: the order in which the down product's operand
+ * loads read it).  Two kernels on `stream`.
  *
  * augq_pack -- one-time weight layout change for augq_forward: w [n_out][n_in]
  * (bf16, row-major) -> w_packed [n_out / 16][n_in / 32][64][8], element

@@ -30,6 +30,15 @@ def _say(*a):
     sys.stdout.flush()
 
 
+def intermediate(ws, M, d_i):
+    """The gated intermediate from the workspace as [M][d_i]: up to 16 tokens
+    the library keeps it chunk-major, [d_i / 8][M][8], beyond that row-major."""
+    a = to_host(ws.view(torch.bfloat16)[:M * d_i])
+    if M <= 16:
+        return a.reshape(d_i // 8, M, 8).transpose(1, 0, 2).reshape(M, d_i)
+    return a.reshape(M, d_i)
+
+
 SHAPES = [
     # M, d_m, d_i, d_out
     (1, 1024, 1024, 256),
@@ -57,7 +66,7 @@ def test_augq_matches_oracle(shape):
     q = dq.augq(h, wg, wu, wd, workspace=ws)
     torch.cuda.synchronize()
     ref_q, ref_a = oracle.augq(*case.widened())
-    act = to_host(ws.view(torch.bfloat16).view(M, d_i))
+    act = intermediate(ws, M, d_i)
     err_a = assert_close(act, ref_a, "bf16", f"augq intermediate {shape}")
     err_q = assert_close(to_host(q), ref_q, "bf16", f"augq {shape}")
     _say(f"  normwise rel err: intermediate {err_a:.2e}, q {err_q:.2e}")
