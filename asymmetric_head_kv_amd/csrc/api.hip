@@ -22,6 +22,16 @@ constexpr int kCUs = 256;             // MI355X compute units
 // hides that latency (512-row chunks: 33.2 us against 30.8).
 constexpr int kWavesPerCUContig = 4;
 constexpr int kWavesPerCUPaged = 8;
+// A contiguous layout whose workgroup loads fewer than kSmallTileElems
+// elements per 64-row tile (the rows of its distinct K heads plus those of
+// its distinct V heads; 48 KiB in bf16) also plans two workgroups per CU, for
+// enough loads in flight: the pages' SIGMA-1.5B attention (32 / 4 / 16 heads,
+// d 64: one K head and four V heads per workgroup, 40 KiB in bf16) takes
+// 21.5 us per 32k step at 256-row chunks against 22.2 at 512, and 14.5
+// against 15.4 at 16k; the 16 / 4 / 16 d_k 64 / d_v 128 layout (72 KiB)
+// loses 2% that way.  Counted in elements, not bytes, so that the plan does
+// not depend on the dtype (the chunk and workspace queries take none).
+constexpr long long kSmallTileElems = 24 << 10;
 constexpr int kMaxChunks = 8192;      // bounds the workspace and the combine's loop
 // Batches of at least kRaggedBatch sequences plan kRaggedOversub times more
 // split workgroups: the host cannot see the lengths (they stay on the
@@ -55,12 +65,14 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int to_status(hipError_t e) { return e == hipSuccess ? DQKV_OK : DQKV_ERR_HIP; }
 
 // Rows per context chunk: enough (sequence, head-quad, chunk) workgroups to
-// give every CU about kWavesPerCUTarget waves (times kRaggedOversub for
-// large batches), in multiples of 64 rows.  H = query heads per wave.
-int plan_chunk_h(int n_q, int H, int batch, int max_ctx, bool paged) {
+// give every CU about the planned waves (times kRaggedOversub for large
+// batches), in multiples of 64 rows.  H = query heads per wave; small =
+// fewer than kSmallTileElems per workgroup tile.
+int plan_chunk_h(int n_q, int H, int batch, int max_ctx, bool paged, bool small) {
   long long quads = (long long)batch * ((n_q / H + 3) / 4);
   if (quads < 1) quads = 1;  // an empty batch launches nothing
-  const int waves = (paged || batch >= kRaggedBatch) ? kWavesPerCUPaged : kWavesPerCUContig;
+  const int waves =
+      (paged || small || batch >= kRaggedBatch) ? kWavesPerCUPaged : kWavesPerCUContig;
   const long long want_wg = (long long)kCUs * waves / 4 *
                             (batch >= kRaggedBatch ? kRaggedOversub : 1);
   long long chunks_per_seq = (want_wg + quads - 1) / quads;
@@ -74,11 +86,17 @@ int plan_chunk_h(int n_q, int H, int batch, int max_ctx, bool paged) {
   return (int)S;
 }
 
-int plan_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx, bool paged) {
+int plan_chunk(int n_q, int n_k, int n_v, int d_k, int d_v, int batch, int max_ctx,
+               bool paged) {
   // Waves per (sequence, chunk): one per query head, or per pair of query
   // heads that share their K and V heads (see the split kernel).
   const int H = (n_q == 2 * n_v && (n_q / n_k) % 2 == 0) ? 2 : 1;
-  return plan_chunk_h(n_q, H, batch, max_ctx, paged);
+  // Elements of one 64-row tile of a four-wave workgroup: the distinct K and
+  // V heads of its 4 H consecutive query heads.
+  const long long heads = 4LL * H, G = n_q / n_k, Gv = n_q / n_v;
+  const long long k_heads = (heads + G - 1) / G, v_heads = (heads + Gv - 1) / Gv;
+  const long long tile = 64LL * (k_heads * d_k + v_heads * d_v);
+  return plan_chunk_h(n_q, H, batch, max_ctx, paged, tile < kSmallTileElems);
 }
 
 int chunks_for(int max_ctx, int S) {
@@ -126,10 +144,10 @@ size_t workspace_bytes(int n_q, int d_v, int batch, int C) {
   return align256(parts * 2 * sizeof(float)) + parts * d_v * sizeof(float);
 }
 
-int resolve_chunk(int n_q, int n_k, int n_v, int batch, int max_ctx, int chunk_tokens,
-                  int* S, bool paged = false) {
+int resolve_chunk(int n_q, int n_k, int n_v, int d_k, int d_v, int batch, int max_ctx,
+                  int chunk_tokens, int* S, bool paged = false) {
   if (chunk_tokens < 0 || chunk_tokens % kMinChunk != 0) return DQKV_ERR_SHAPE;
-  *S = chunk_tokens ? chunk_tokens : plan_chunk(n_q, n_k, n_v, batch, max_ctx, paged);
+  *S = chunk_tokens ? chunk_tokens : plan_chunk(n_q, n_k, n_v, d_k, d_v, batch, max_ctx, paged);
   if (chunks_for(max_ctx, *S) > kMaxChunks) return DQKV_ERR_UNSUPPORTED;
   return DQKV_OK;
 }
@@ -244,7 +262,7 @@ int32_t diffqkv_decode_chunk(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
   int st = check_heads(n_q, n_k, n_v, d_k, d_v);
   if (st) return st;
   if (batch < 0 || max_ctx < 0) return DQKV_ERR_SHAPE;
-  return resolve_chunk(n_q, n_k, n_v, batch, max_ctx, 0, chunk_tokens);
+  return resolve_chunk(n_q, n_k, n_v, d_k, d_v, batch, max_ctx, 0, chunk_tokens);
 }
 
 int32_t diffqkv_decode_workspace(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k,
@@ -257,9 +275,9 @@ int32_t diffqkv_decode_workspace(int32_t n_q, int32_t n_k, int32_t n_v, int32_t 
   // With the automatic choice: enough for the contiguous and the paged plan
   // (the paged one never has fewer chunks).
   int S = 0, Sp = 0;
-  st = resolve_chunk(n_q, n_k, n_v, batch, max_ctx, chunk_tokens, &S);
+  st = resolve_chunk(n_q, n_k, n_v, d_k, d_v, batch, max_ctx, chunk_tokens, &S);
   if (st) return st;
-  st = resolve_chunk(n_q, n_k, n_v, batch, max_ctx, chunk_tokens, &Sp, true);
+  st = resolve_chunk(n_q, n_k, n_v, d_k, d_v, batch, max_ctx, chunk_tokens, &Sp, true);
   if (st) return st;
   *bytes = workspace_bytes(n_q, d_v, batch, chunks_for(max_ctx, S < Sp ? S : Sp));
   return DQKV_OK;
@@ -322,7 +340,7 @@ static int prepare_decode(int32_t n_q, int32_t n_k, int32_t n_v, int32_t d_k, in
       (need_out && !aligned16(out)) || (check_ws_ptr && !aligned16(workspace)))
     return DQKV_ERR_ALIGN;
   int S = 0;
-  st = resolve_chunk(n_q, n_k, n_v, batch, max_ctx, chunk_tokens, &S, paged);
+  st = resolve_chunk(n_q, n_k, n_v, d_k, d_v, batch, max_ctx, chunk_tokens, &S, paged);
   if (st) return st;
   const int C = chunks_for(max_ctx, S);
   if ((long long)(n_q + 3) / 4 > 65535) return DQKV_ERR_UNSUPPORTED;

@@ -119,6 +119,15 @@ def test_workspace_and_chunk_plan(lib):
     # plan about seven times more chunks than a small batch would.
     assert 32768 // dq.decode_chunk(16, 4, 16, 64, 128, 1, 32768) == 64
     assert -(-32769 // dq.decode_chunk(16, 4, 16, 64, 128, 16, 32769)) >= 32
+    # Layouts whose four-wave workgroup loads under 24Ki elements per 64-row
+    # tile plan two workgroups per CU: the pages' SIGMA-1.5B attention (32 /
+    # 4 / 16 heads, d 64: one K head and four V heads, 20Ki elements) gets
+    # twice the chunks of one round; the standard GQA model (32 / 16 / 16,
+    # four K and four V heads, 32Ki) and the 16 / 4 / 16 layout (36Ki) keep
+    # one workgroup per CU.  The plan does not depend on the dtype.
+    assert 32768 // dq.decode_chunk(32, 4, 16, 64, 64, 1, 32768) == 128
+    assert 32768 // dq.decode_chunk(32, 16, 16, 64, 64, 1, 32768) == 64
+    assert 16384 // dq.decode_chunk(32, 4, 16, 64, 64, 1, 16384) == 128
     # Explicit chunk lengths are honoured.
     assert dq.decode_workspace_bytes(16, 4, 16, 64, 128, 1, 4096, 64) == \
         -(-16 * 64 * 8 // 256) * 256 + 16 * 64 * 128 * 4
