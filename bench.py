@@ -241,6 +241,18 @@ class DecodeBench:
             self.lse.data_ptr(), self.chunk, self.ws.data_ptr(), self.ws_bytes, self._stream())
         assert st == 0, st
 
+    def paged_selective_step(self, r):
+        """The selective-V step (fused append, logits, top-k, V gather) over
+        paged caches (after setup_selective and setup_paged)."""
+        kp, vp = self.pages[r]
+        st = self.lib.diffqkv_decode_selective_paged(
+            *self.shape, self.dtype_code, self.B, self.page_rows, self.num_pages,
+            self.max_blocks, self.max_ctx, self.case.scale, self.top_k, self.q.data_ptr(),
+            self.k_new.data_ptr(), self.v_new.data_ptr(), kp.data_ptr(), vp.data_ptr(),
+            self.block_table.data_ptr(), self.ctx_t.data_ptr(), self.sel_out.data_ptr(),
+            self.lse.data_ptr(), None, self.sel_ws.data_ptr(), self.sel_ws_bytes, self._stream())
+        assert st == 0, st
+
     def setup_compat(self):
         """kv_group_sharing copies of every replica (n_h = max(n_k, n_v) heads
         on both sides) and the time of one expansion."""
@@ -515,10 +527,37 @@ def prefill_bench(steps: int = 10):
     pairs = sum(L - T + r + 1 for r in range(T))
     flops = pairs * case.n_q * 2 * (case.d_k + case.d_v)
     tflops = flops / (ms * 1e-3) / 1e12
-    return {"workload": "prefill2k_on_30k", "us_per_call": round(ms * 1e3, 2),
-            "algorithmic_gflop": round(flops / 1e9, 2), "tflops": round(tflops, 1),
-            "bound": "mfma", "peak_tflops": BF16_PEAK_TFLOPS,
-            "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    rec = {"workload": "prefill2k_on_30k", "us_per_call": round(ms * 1e3, 2),
+           "algorithmic_gflop": round(flops / 1e9, 2), "tflops": round(tflops, 1),
+           "bound": "mfma", "peak_tflops": BF16_PEAK_TFLOPS,
+           "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+    # The same call over a paged cache: 64-row pages in a seeded random order.
+    P = 64
+    nblk = -(-case.l_cap // P)
+    perm = torch.randperm(nblk, generator=torch.Generator().manual_seed(0)).to(dev)
+
+    def to_pages(c):
+        h, d = c.shape[1], c.shape[3]
+        x = torch.zeros((h, nblk * P, d), dtype=c.dtype, device=dev)
+        x[:, :case.l_cap] = c[0]
+        pg = torch.empty((nblk, h, P, d), dtype=c.dtype, device=dev)
+        pg[perm] = x.view(h, nblk, P, d).permute(1, 0, 2, 3)
+        return pg
+
+    kp, vp = to_pages(k), to_pages(v)
+    table = perm.to(torch.int32).view(1, nblk)
+    for _ in range(2):
+        dq.prefill_paged(q, kp, vp, table, ctx, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        dq.prefill_paged(q, kp, vp, table, ctx, out=out, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_p = t0.elapsed_time(t1) / steps
+    rec["paged"] = {"page_rows": P, "us_per_call": round(ms_p * 1e3, 2),
+                    "time_over_contiguous": round(ms_p / ms, 3)}
+    return rec
 
 
 def augq_bench(steps: int = 200):
@@ -837,6 +876,12 @@ def main():
                            "GBps": round(bench.alg_bytes_step / (ms_pg * 1e-3) / 1e9, 1),
                            "time_over_contiguous": round(ms_pg / ms, 3),
                            "pages": "each sequence's blocks in a seeded random page order"}
+        if args.selective_k > 0:
+            ms_ps, _ = bench.time_steps(args.steps, args.warmup, args.eager,
+                                        bench.paged_selective_step)
+            log(f"paged selective-V step {ms_ps * 1e3:.2f} us")
+            result["paged"]["selective_us_per_step"] = round(ms_ps * 1e3, 2)
+            result["paged"]["selective_time_over_contiguous"] = round(ms_ps / ms_sel, 3)
         bench.pages = None
     n_q_, n_k_, n_v_, d_k_, d_v_ = bench.shape
     if not args.no_compat and not args.kernel_only and n_k_ != n_v_:
