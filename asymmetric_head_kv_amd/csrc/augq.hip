@@ -39,15 +39,23 @@ typedef __bf16 aq_bf16x8 __attribute__((ext_vector_type(8)));
 // -- so that the 16 x 32 A operand of one step is M x 64 contiguous bytes (a
 // row-major A gives 16-byte pieces of rows K elements apart, and every load
 // touches a cache line per row).  The gate/up product writes the gated
-// intermediate this way for the down product.
+// intermediate this way for the down product.  STAGE_A (MT = 1, row-major A,
+// slices of at most 128 columns in one round; chosen for more than 8 rows):
+// each wave loads its 16 x kq slice of A as whole 2 kq-byte row pieces, four
+// rows per load, into its own LDS rows and reads the operands from there (16
+// tokens: 14.7 -> 14.2 us per call; up to 8 rows the direct loads are
+// 0.1-0.2 us faster).
 template <int MT, bool SWIGLU, int W, int STEPS, bool CHUNKED_IN = false,
-          bool CHUNKED_OUT = false>
+          bool CHUNKED_OUT = false, bool STAGE_A = false>
 __global__ __launch_bounds__(64 * W) void augq_gemm_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ B0, const bf16* __restrict__ B1,
     bf16* __restrict__ C, int M, int N, int K) {
   static_assert(MT == 1 || !(CHUNKED_IN || CHUNKED_OUT), "chunked layout: one row tile");
+  static_assert(!STAGE_A || (MT == 1 && !CHUNKED_IN), "staging: one row tile, row-major A");
   constexpr int NP = SWIGLU ? 2 : 1;  // products per tile
   __shared__ f32x4 part[W - 1][MT][NP][64];
+  constexpr int kSC = 128, kSP = kSC + 8;  // staged columns per row, row pitch (bf16)
+  __shared__ __align__(16) __bf16 astage[STAGE_A ? W : 1][16][kSP];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16 * MT;
@@ -76,8 +84,19 @@ __global__ __launch_bounds__(64 * W) void augq_gemm_kernel(
 #pragma unroll
     for (int p = 0; p < NP; ++p) acc[mt][p] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const bool staged = STAGE_A && kq <= kSC && kq <= 32 * STEPS;  // checked on the host too
   for (int k0 = kbeg; k0 < kend; k0 += 32 * STEPS) {
     u32x4 bv[NP][STEPS], av[MT][STEPS];
+    u32x4 sv[4];
+    const int ncr = kq / 8;  // 16-byte chunks per staged row
+    if (staged) {  // one round (kq <= 32 STEPS): the wave's whole A slice
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = i * 64 + lane, row = idx / ncr, c = idx % ncr;
+        sv[i] = idx < 16 * ncr && m0 + row < M ? load16(A + (size_t)(m0 + row) * K + kbeg + 8 * c)
+                                                : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
       const bool ok = k0 + 32 * s < kend;
@@ -88,8 +107,21 @@ __global__ __launch_bounds__(64 * W) void augq_gemm_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const size_t ao = CHUNKED_IN ? (size_t)((k0 + 32 * s) / 8) * M * 8 : (size_t)(k0 + 32 * s);
-        av[mt][s] = ok && arow[mt] ? load16(ap[mt] + ao) : u32x4{0u, 0u, 0u, 0u};
+        av[mt][s] = !staged && ok && arow[mt] ? load16(ap[mt] + ao) : u32x4{0u, 0u, 0u, 0u};
       }
+    }
+    if (staged) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = i * 64 + lane, row = idx / ncr, c = idx % ncr;
+        if (idx < 16 * ncr)
+          *reinterpret_cast<u32x4*>(&astage[STAGE_A ? wave : 0][row][8 * c]) = sv[i];
+      }
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s)
+        if (32 * s < kq)
+          av[0][s] =
+              *reinterpret_cast<const u32x4*>(&astage[STAGE_A ? wave : 0][l16][32 * s + 8 * kg]);
     }
 #pragma unroll
     for (int s = 0; s < STEPS; ++s)
@@ -141,13 +173,12 @@ __global__ __launch_bounds__(64 * W) void augq_gemm_kernel(
 }
 
 template <int MT, bool SWIGLU, int W, int STEPS, bool CHUNKED_IN = false,
-          bool CHUNKED_OUT = false>
+          bool CHUNKED_OUT = false, bool STAGE_A = false>
 static hipError_t launch_gemm(const bf16* A, const bf16* B0, const bf16* B1, bf16* C, int M,
                               int N, int K, hipStream_t stream) {
   dim3 grid(N / 16, (M + 16 * MT - 1) / (16 * MT));
-  hipLaunchKernelGGL((augq_gemm_kernel<MT, SWIGLU, W, STEPS, CHUNKED_IN, CHUNKED_OUT>), grid,
-                     dim3(64 * W), 0, stream, A,
-                     B0, B1, C, M, N, K);
+  hipLaunchKernelGGL((augq_gemm_kernel<MT, SWIGLU, W, STEPS, CHUNKED_IN, CHUNKED_OUT, STAGE_A>),
+                     grid, dim3(64 * W), 0, stream, A, B0, B1, C, M, N, K);
   return hipGetLastError();
 }
 
@@ -356,7 +387,15 @@ static hipError_t launch_tiled(const bf16* A, const bf16* B0, const bf16* B1, bf
 template <bool SWIGLU>
 static hipError_t gemm(const bf16* A, const bf16* B0, const bf16* B1, bf16* C, int M, int N,
                        int K, hipStream_t stream) {
-  if (M <= 16) return launch_gemm<1, SWIGLU, 16, 8, !SWIGLU, SWIGLU>(A, B0, B1, C, M, N, K, stream);
+  if (M <= 16) {
+    // The staged gate/up product takes 4 steps per round (d_m = 2048: one
+    // round, registers left for the staging).
+    if constexpr (SWIGLU) {
+      if (M > 8 && K / 16 <= 128)
+        return launch_gemm<1, true, 16, 4, false, true, true>(A, B0, B1, C, M, N, K, stream);
+    }
+    return launch_gemm<1, SWIGLU, 16, 8, !SWIGLU, SWIGLU>(A, B0, B1, C, M, N, K, stream);
+  }
   if (M > 64 && K % 64 == 0) {
     const bool big = M >= 1024;
     if constexpr (SWIGLU) {

@@ -43,6 +43,7 @@ SHAPES = [
     # M, d_m, d_i, d_out
     (1, 1024, 1024, 256),
     (5, 2048, 3072, 2048),     # SIGMA-1.5B, a few decode tokens
+    (12, 2048, 3072, 2048),    # the gate/up operand staged through LDS, rows 12-15 empty
     (16, 1024, 2048, 512),
     (17, 1024, 1024, 64),      # first size that takes 64-row workgroups
     (64, 1024, 2048, 128),     # last size on the 64-row workgroups
