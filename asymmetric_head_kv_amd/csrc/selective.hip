@@ -72,8 +72,10 @@ __device__ __forceinline__ uint64_t lanes_below() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Exclusive prefix sum of v over the 256 threads of the block, in thread
-// order; *total receives the block's sum.  Uses red[0..3]; ends synchronised.
+// Exclusive prefix sum of v over the NT threads of the block, in thread
+// order; *total receives the block's sum.  Uses red[0 .. NT/64 - 1]; ends
+// synchronised.
+template <int NT = kSelThreads>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = v;
@@ -86,7 +88,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int* total)
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const int t = red[w];
     before += w < wave ? t : 0;
     tot += t;
@@ -107,10 +109,12 @@ struct Threshold {
 // that prefix number k - krem.  A pass whose chosen bin holds exactly krem
 // keys ends the search: every key with that prefix is taken, so the
 // threshold is the prefix's lowest key minus one with no equal keys taken
-// (the same set as the remaining passes would give).  hist: kBins LDS
-// words; red: 8 LDS ints.
-template <class KeyF>
+// (the same set as the remaining passes would give).  NT threads; hist: kBins
+// LDS words; red: 2 NT/64 LDS ints (the digit search uses red[NT/64 ..
+// NT/64 + 2]).
+template <int NT = kSelThreads, class KeyF>
 __device__ Threshold block_select_threshold(KeyF key, int n, int k, uint32_t* hist, int* red) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
@@ -118,17 +122,17 @@ __device__ Threshold block_select_threshold(KeyF key, int n, int k, uint32_t* hi
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-    for (int d = tid; d < kBins; d += kSelThreads) hist[d] = 0u;
+    for (int d = tid; d < kBins; d += NT) hist[d] = 0u;
     __syncthreads();
-    for (int x = tid; x < n; x += kSelThreads) {
+    for (int x = tid; x < n; x += NT) {
       const uint32_t kk = key(x);
       if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & dmask], 1u);
     }
     __syncthreads();
-    // Thread t owns bins kBins-1-8t down to kBins-8-8t: bins in descending
-    // order across the block, so the exclusive scan counts the keys in
-    // higher bins.
-    constexpr int BPT = kBins / kSelThreads;
+    // Thread t owns bins kBins-1-BPT t down to kBins-BPT-BPT t: bins in
+    // descending order across the block, so the exclusive scan counts the
+    // keys in higher bins.
+    constexpr int BPT = kBins / NT;
     int cnt[BPT], own = 0;
 #pragma unroll
     for (int e = 0; e < BPT; ++e) {
@@ -136,42 +140,44 @@ __device__ Threshold block_select_threshold(KeyF key, int n, int k, uint32_t* hi
       own += cnt[e];
     }
     int total;
-    const int above = block_exclusive_scan(own, red, &total);
+    const int above = block_exclusive_scan<NT>(own, red, &total);
     if (above < krem && krem <= above + own) {  // exactly one thread
       int run = above;
 #pragma unroll
       for (int e = 0; e < BPT; ++e) {
         if (run + cnt[e] >= krem) {
-          red[4] = kBins - 1 - BPT * tid - e;
-          red[5] = krem - run;
-          red[6] = cnt[e] == krem - run;
+          red[NW] = kBins - 1 - BPT * tid - e;
+          red[NW + 1] = krem - run;
+          red[NW + 2] = cnt[e] == krem - run;
           break;
         }
         run += cnt[e];
       }
     }
     __syncthreads();
-    const uint32_t digit = (uint32_t)red[4];
-    krem = red[5];
+    const uint32_t digit = (uint32_t)red[NW];
+    krem = red[NW + 1];
     prefix |= digit << shift;
     pmask |= dmask << shift;
-    if (red[6] != 0 && prefix != 0u) {  // the whole bin is taken
-      __syncthreads();  // red[4..6] are rewritten by the next caller
+    if (red[NW + 2] != 0 && prefix != 0u) {  // the whole bin is taken
+      __syncthreads();  // red[NW .. NW + 2] are rewritten by the next caller
       return Threshold{prefix - 1u, 0};
     }
   }
-  __syncthreads();  // red[4..6] are rewritten by the next caller
+  __syncthreads();  // red[NW .. NW + 2] are rewritten by the next caller
   return Threshold{prefix, krem};
 }
 
 // Calls emit(pos, x) for the k selected positions x (key above the
 // threshold, or equal to it and among the first need_eq such in index
-// order), with pos = rank of x among the selected in index order.  Each wave
-// walks one contiguous quarter of [0, n) in 64-element steps.
-template <class KeyF, class EmitF>
+// order), with pos = rank of x among the selected in index order.  Each of
+// the NT/64 waves walks one contiguous segment of [0, n) in 64-element
+// steps; red: 2 NT/64 ints.
+template <int NT = kSelThreads, class KeyF, class EmitF>
 __device__ void block_compact(KeyF key, int n, Threshold th, int* red, EmitF emit) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int seg = ((n + 4 * 64 - 1) / (4 * 64)) * 64;
+  const int seg = ((n + NW * 64 - 1) / (NW * 64)) * 64;
   const int lo = min(n, wave * seg), hi = min(n, lo + seg);
   int gt = 0, eq = 0;
   for (int x0 = lo; x0 < hi; x0 += 64) {
@@ -182,13 +188,13 @@ __device__ void block_compact(KeyF key, int n, Threshold th, int* red, EmitF emi
   }
   if (lane == 0) {
     red[wave] = gt;
-    red[4 + wave] = eq;
+    red[NW + wave] = eq;
   }
   __syncthreads();
   int gt_before = 0, eq_before = 0;
   for (int w = 0; w < wave; ++w) {
     gt_before += red[w];
-    eq_before += red[4 + w];
+    eq_before += red[NW + w];
   }
   __syncthreads();
   int pos0 = gt_before + min(eq_before, th.need_eq);
@@ -207,10 +213,11 @@ __device__ void block_compact(KeyF key, int n, Threshold th, int* red, EmitF emi
   }
 }
 
-// Register-resident variants for up to kSelThreads * E keys: wave w, lane l
-// holds elements w * 64 E + 64 e + l (e < E) in its registers, so each wave
-// owns a contiguous quarter and every load of a wave is 64 consecutive
-// elements.  One round of loads, then every pass works from registers.
+// Register-resident variants for up to NT * E keys (NT threads): wave w,
+// lane l holds elements w * 64 E + 64 e + l (e < E) in its registers, so
+// each wave owns a contiguous segment and every load of a wave is 64
+// consecutive elements.  One round of loads, then every pass works from
+// registers.
 
 template <int E>
 __device__ __forceinline__ int reg_index(int e) {
@@ -218,10 +225,12 @@ __device__ __forceinline__ int reg_index(int e) {
 }
 
 // hist: three kBins-word histograms (one per digit pass), zeroed and made
-// visible by a barrier before the call.  Ends early as the block variant.
-template <int E>
+// visible by a barrier before the call; red: 2 NT/64 ints.  Ends early as
+// the block variant.
+template <int E, int NT = kSelThreads>
 __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k,
                                           uint32_t* hist, int* red) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
@@ -235,7 +244,7 @@ __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k
       if (reg_index<E>(e) < n && (key[e] & pmask) == prefix)
         atomicAdd(&h[(key[e] >> shift) & dmask], 1u);
     __syncthreads();
-    constexpr int BPT = kBins / kSelThreads;
+    constexpr int BPT = kBins / NT;
     int cnt[BPT], own = 0;
 #pragma unroll
     for (int e = 0; e < BPT; ++e) {
@@ -243,25 +252,25 @@ __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k
       own += cnt[e];
     }
     int total;
-    const int above = block_exclusive_scan(own, red, &total);
+    const int above = block_exclusive_scan<NT>(own, red, &total);
     if (above < krem && krem <= above + own) {
       int run = above;
 #pragma unroll
       for (int e = 0; e < BPT; ++e) {
         if (run + cnt[e] >= krem) {
-          red[4] = kBins - 1 - BPT * tid - e;
-          red[5] = krem - run;
-          red[6] = cnt[e] == krem - run;
+          red[NW] = kBins - 1 - BPT * tid - e;
+          red[NW + 1] = krem - run;
+          red[NW + 2] = cnt[e] == krem - run;
           break;
         }
         run += cnt[e];
       }
     }
     __syncthreads();
-    prefix |= (uint32_t)red[4] << shift;
+    prefix |= (uint32_t)red[NW] << shift;
     pmask |= dmask << shift;
-    krem = red[5];
-    if (red[6] != 0 && prefix != 0u) {  // the whole bin is taken (as above)
+    krem = red[NW + 1];
+    if (red[NW + 2] != 0 && prefix != 0u) {  // the whole bin is taken (as above)
       __syncthreads();
       return Threshold{prefix - 1u, 0};
     }
@@ -270,15 +279,18 @@ __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k
   return Threshold{prefix, krem};
 }
 
+template <int NT = kSelThreads>
 __device__ __forceinline__ void clear_hists(uint32_t* hist) {
   u32x4* h = reinterpret_cast<u32x4*>(hist);
-  for (int x = threadIdx.x; x < 3 * kBins / 4; x += kSelThreads) h[x] = u32x4{0u, 0u, 0u, 0u};
+  for (int x = threadIdx.x; x < 3 * kBins / 4; x += NT) h[x] = u32x4{0u, 0u, 0u, 0u};
 }
 
-// emit(pos, e) for every selected register slot e, pos = rank in index order.
-template <int E, class EmitF>
+// emit(pos, e) for every selected register slot e, pos = rank in index order
+// (NT threads; red: 2 NT/64 ints).
+template <int E, int NT = kSelThreads, class EmitF>
 __device__ __forceinline__ void reg_compact(const uint32_t (&key)[E], int n, Threshold th,
                                             int* red, EmitF emit) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int gt = 0, eq = 0;
 #pragma unroll
@@ -289,13 +301,13 @@ __device__ __forceinline__ void reg_compact(const uint32_t (&key)[E], int n, Thr
   }
   if (lane == 0) {
     red[wave] = gt;
-    red[4 + wave] = eq;
+    red[NW + wave] = eq;
   }
   __syncthreads();
   int gt_before = 0, eq_before = 0;
   for (int w = 0; w < wave; ++w) {
     gt_before += red[w];
-    eq_before += red[4 + w];
+    eq_before += red[NW + w];
   }
   __syncthreads();
   int pos0 = gt_before + min(eq_before, th.need_eq);
@@ -314,7 +326,6 @@ __device__ __forceinline__ void reg_compact(const uint32_t (&key)[E], int n, Thr
   }
 }
 
-constexpr int kSelE = kSelRows / kSelThreads;  // keys per thread of the longest range
 
 // ------------------------------------------------------------ 1. scores
 
@@ -567,9 +578,9 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
 
 // ------------------------------------------ 3. final selection and gather
 
-// E: candidate keys per thread held in registers (E * kSelThreads of them).
-template <typename T, int DV, int E>
-__global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
+// E: candidate keys per thread held in registers (E * NT of them), NT threads.
+template <typename T, int DV, int E, int NT>
+__global__ __launch_bounds__(NT) void sel_gather_kernel(
     const T* vc, const int32_t* __restrict__ ctx_len, const float* __restrict__ range_ml,
     const float* __restrict__ cand_s, const int32_t* __restrict__ cand_i, T* __restrict__ out,
     float* __restrict__ lse, int32_t* __restrict__ sel_idx, int n_q, int n_v, int l_cap,
@@ -577,10 +588,10 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
     PageMap pm) {
   constexpr int EPL = Elem<T>::kPer16;
   constexpr int LPR = DV / EPL;               // lanes per V row
-  constexpr int RPP = kSelThreads / LPR;      // V rows per pass of the block
+  constexpr int RPP = NT / LPR;               // V rows per pass of the block
   constexpr int U = 128 / RPP < 1 ? 1 : (128 / RPP > 8 ? 8 : 128 / RPP);  // passes in flight
   __shared__ __align__(16) uint32_t hist[3 * kBins];
-  __shared__ int red[8];
+  __shared__ int red[2 * (NT / 64)];
   __shared__ int32_t sel_j[kMaxTopK];
   __shared__ float sel_w[kMaxTopK];
   __shared__ float part[RPP][DV + 4];
@@ -624,7 +635,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
   const int nr = (L + range_rows - 1) / range_rows;
   const int n_c = nr == 0 ? 0 : (nr - 1) * top_k + min(top_k, L - (nr - 1) * range_rows);
   const int kk = min(top_k, L);
-  const bool in_regs = n_c <= E * kSelThreads;
+  const bool in_regs = n_c <= E * NT;
   if (in_regs) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -635,7 +646,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
     }
   }
 
-  clear_hists(hist);
+  clear_hists<NT>(hist);
   // Softmax normaliser over all L rows from the ranges' (max, sum); every
   // wave computes it alike, so no barrier is needed.
   float M = lane < nr ? ml_m : -INFINITY;
@@ -662,8 +673,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
       uint32_t key[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) key[e] = order_key(s[e]);
-      const Threshold th = reg_select_threshold<E>(key, n_c, kk, hist, red);
-      reg_compact<E>(key, n_c, th, red, take);
+      const Threshold th = reg_select_threshold<E, NT>(key, n_c, kk, hist, red);
+      reg_compact<E, NT>(key, n_c, th, red, take);
     }
   } else {  // more candidates than registers hold: passes over global memory
     auto take = [&](int pos, int p) {
@@ -673,12 +684,12 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
       }
     };
     auto key = [&](int p) { return order_key(cs[p]); };
-    const Threshold th = block_select_threshold(key, n_c, kk, hist, red);
-    block_compact(key, n_c, th, red, take);
+    const Threshold th = block_select_threshold<NT>(key, n_c, kk, hist, red);
+    block_compact<NT>(key, n_c, th, red, take);
   }
   __syncthreads();
   if (sel_idx != nullptr)
-    for (int p = tid; p < top_k; p += kSelThreads)
+    for (int p = tid; p < top_k; p += NT)
       sel_idx[head * top_k + p] = p < kk ? sel_j[p] : -1;
 
   // o = sum over the selected rows of w_j V_j: LPR lanes per row, RPP rows
@@ -714,7 +725,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_gather_kernel(
 #pragma unroll
   for (int e = 0; e < EPL; ++e) part[vr][vl * EPL + e] = acc[e];
   __syncthreads();
-  for (int d = tid; d < DV; d += kSelThreads) {
+  for (int d = tid; d < DV; d += NT) {
     float o = 0.f;
     for (int r = 0; r < RPP; ++r) o += part[r][d];
     out[head * DV + d] = Elem<T>::from_f32(o);
@@ -760,21 +771,26 @@ static hipError_t launch_score_t(const SelectiveArgs& a) {
   return hipErrorInvalidValue;
 }
 
+// Threads of the final selection and gather workgroup (selective step,
+// same process: 32k 22.5 / 21.4 / 22.0 us at 256 / 512 / 1024 threads,
+// 4 x 64k 56.3 / 54.9 / 55.8, 16 sequences of 4k..32k 71.3 / 70.1 / 71.1).
+constexpr int kGatherThreads = 512;
+
+template <typename T, int DV, int E>
+static void launch_gather_e(const SelectiveArgs& a) {
+  hipLaunchKernelGGL((sel_gather_kernel<T, DV, E, kGatherThreads>), dim3(a.n_q, a.batch),
+                     dim3(kGatherThreads), 0, a.stream, (const T*)a.v_cache, a.ctx_len,
+                     a.range_ml, a.cand_s, a.cand_i, (T*)a.out, a.lse, a.sel_idx, a.n_q, a.n_v,
+                     a.l_cap, a.max_ctx, a.n_ranges, a.range_rows, a.top_k, (const T*)a.v_new,
+                     (T*)a.v_cache, a.pages);
+}
+
 template <typename T, int DV>
 static hipError_t launch_gather_t(const SelectiveArgs& a) {
-  // Half the registers when every candidate fits in 8 per thread.
-  if ((long long)a.n_ranges * a.top_k <= 8 * kSelThreads)
-    hipLaunchKernelGGL((sel_gather_kernel<T, DV, 8>), dim3(a.n_q, a.batch), dim3(kSelThreads),
-                       0, a.stream, (const T*)a.v_cache, a.ctx_len, a.range_ml, a.cand_s,
-                       a.cand_i, (T*)a.out, a.lse, a.sel_idx, a.n_q, a.n_v, a.l_cap, a.max_ctx,
-                       a.n_ranges, a.range_rows, a.top_k, (const T*)a.v_new, (T*)a.v_cache,
-                       a.pages);
-  else
-    hipLaunchKernelGGL((sel_gather_kernel<T, DV, kSelE>), dim3(a.n_q, a.batch),
-                       dim3(kSelThreads), 0, a.stream, (const T*)a.v_cache, a.ctx_len,
-                       a.range_ml, a.cand_s, a.cand_i, (T*)a.out, a.lse, a.sel_idx, a.n_q,
-                       a.n_v, a.l_cap, a.max_ctx, a.n_ranges, a.range_rows, a.top_k,
-                       (const T*)a.v_new, (T*)a.v_cache, a.pages);
+  // Half the registers when every candidate fits in 2048 slots.
+  constexpr int E_SMALL = 2048 / kGatherThreads, E_LARGE = 4096 / kGatherThreads;
+  if ((long long)a.n_ranges * a.top_k <= 2048) launch_gather_e<T, DV, E_SMALL>(a);
+  else launch_gather_e<T, DV, E_LARGE>(a);
   return hipGetLastError();
 }
 
