@@ -493,15 +493,16 @@ __global__ __launch_bounds__(256) void sel_score_mfma_kernel(
 // One workgroup per (query head, range of RS rows); candidates of range rg
 // are written at [rg * top_k, rg * top_k + min(top_k, rows)), so a head's
 // candidate list is contiguous and in ascending row order.
-template <int RS>
-__global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
+template <int RS, int NT>
+__global__ __launch_bounds__(NT) void sel_local_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_len,
     float* __restrict__ range_ml, float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
     int n_q, int l_cap, int max_ctx, int ld_s, int n_ranges, int top_k) {
-  constexpr int E = RS / kSelThreads;  // keys per thread
+  constexpr int E = RS / NT;  // keys per thread
+  constexpr int NW = NT / 64;
   __shared__ __align__(16) uint32_t hist[3 * kBins];
-  __shared__ int red[8];
-  __shared__ float wm[4], wl[4];
+  __shared__ int red[2 * NW];
+  __shared__ float wm[NW], wl[NW];
   const int rg = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int L = ctx_len[b];
@@ -527,7 +528,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if (reg_index<E>(e) >= rows) s[e] = -INFINITY;
-  clear_hists(hist);
+  clear_hists<NT>(hist);
   // The range's max and sum of 2^(s - max): per wave, then over the waves.
   float m = s[0];
 #pragma unroll
@@ -544,9 +545,12 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
   __syncthreads();
   const size_t slot = ((size_t)b * n_q + i) * n_ranges + rg;
   if (threadIdx.x == 0) {
-    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+    float M = wm[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, wm[w]);
     float Z = 0.f;
-    for (int w = 0; w < 4; ++w) Z += wl[w] > 0.f ? wl[w] * fast_exp2(wm[w] - M) : 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Z += wl[w] > 0.f ? wl[w] * fast_exp2(wm[w] - M) : 0.f;
     range_ml[2 * slot] = M;
     range_ml[2 * slot + 1] = Z;
   }
@@ -567,8 +571,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_local_kernel(
   uint32_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = order_key(s[e]);
-  const Threshold th = reg_select_threshold<E>(key, rows, top_k, hist, red);
-  reg_compact<E>(key, rows, th, red, [&](int pos, int e) {
+  const Threshold th = reg_select_threshold<E, NT>(key, rows, top_k, hist, red);
+  reg_compact<E, NT>(key, rows, th, red, [&](int pos, int e) {
     if (pos < top_k) {
       cs[pos] = s[e];
       ci[pos] = j0 + reg_index<E>(e);
@@ -771,6 +775,12 @@ static hipError_t launch_score_t(const SelectiveArgs& a) {
   return hipErrorInvalidValue;
 }
 
+// Threads of a range-selection workgroup: 512 for the short ranges (planned
+// when the long ones leave CUs idle; 32k step 21.2 -> 20.7 us), 256 for the
+// long ones, where more workgroups share each CU (4 x 64k 54.8 against 56.0
+// at 512; 16 sequences of 4k..32k 70.5 against 72.1).
+constexpr int kLocalThreadsShort = 512, kLocalThreadsLong = 256;
+
 // Threads of the final selection and gather workgroup (selective step,
 // same process: 32k 22.5 / 21.4 / 22.0 us at 256 / 512 / 1024 threads,
 // 4 x 64k 56.3 / 54.9 / 55.8, 16 sequences of 4k..32k 71.3 / 70.1 / 71.1).
@@ -840,15 +850,15 @@ hipError_t launch_decode_selective(const SelectiveArgs& a) {
   hipError_t e = a.bf16 ? score_dk<bf16>(a) : score_dk<float>(a);
   if (e != hipSuccess) return e;
   if (a.range_rows == kSelRowsShort)
-    hipLaunchKernelGGL(sel_local_kernel<kSelRowsShort>, dim3(a.n_ranges, a.n_q, a.batch),
-                       dim3(kSelThreads), 0, a.stream, a.scores, a.ctx_len, a.range_ml,
-                       a.cand_s, a.cand_i, a.n_q, a.l_cap, a.max_ctx, a.ld_s, a.n_ranges,
-                       a.top_k);
+    hipLaunchKernelGGL((sel_local_kernel<kSelRowsShort, kLocalThreadsShort>),
+                       dim3(a.n_ranges, a.n_q, a.batch), dim3(kLocalThreadsShort), 0, a.stream,
+                       a.scores, a.ctx_len, a.range_ml, a.cand_s, a.cand_i, a.n_q, a.l_cap,
+                       a.max_ctx, a.ld_s, a.n_ranges, a.top_k);
   else
-    hipLaunchKernelGGL(sel_local_kernel<kSelRows>, dim3(a.n_ranges, a.n_q, a.batch),
-                       dim3(kSelThreads), 0, a.stream, a.scores, a.ctx_len, a.range_ml,
-                       a.cand_s, a.cand_i, a.n_q, a.l_cap, a.max_ctx, a.ld_s, a.n_ranges,
-                       a.top_k);
+    hipLaunchKernelGGL((sel_local_kernel<kSelRows, kLocalThreadsLong>),
+                       dim3(a.n_ranges, a.n_q, a.batch), dim3(kLocalThreadsLong), 0, a.stream,
+                       a.scores, a.ctx_len, a.range_ml, a.cand_s, a.cand_i, a.n_q, a.l_cap,
+                       a.max_ctx, a.ld_s, a.n_ranges, a.top_k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return a.bf16 ? gather_dv<bf16>(a) : gather_dv<float>(a);
