@@ -440,18 +440,29 @@ def pmc_traffic(workload: str):
         return None
 
 
-def decode_record(name: str, steps: int, warmup: int, chunk: int = 0) -> dict:
+def decode_record(name: str, steps: int, warmup: int, chunk: int = 0,
+                  selective_k: int = 0) -> dict:
     """Step time (split with the fused append + combine, graph replay over
-    cache replicas) and the split kernel alone, for one decode workload."""
+    cache replicas) and the split kernel alone, for one decode workload; with
+    selective_k > 0 also the selective-V step on the same caches."""
     bn = DecodeBench(name, chunk)
     ms, graphed = bn.time_steps(steps, warmup)
+    spread = bn.step_pct_us
     split_ms, comb_ms = bn.time_kernels(steps)
+    sel = None
+    if selective_k > 0:
+        bn.setup_selective(selective_k)
+        ms_sel, _ = bn.time_steps(steps, warmup, fn=bn.selective_step)
+        sel = {"top_k": selective_k, "us_per_step": round(ms_sel * 1e3, 2),
+               "alg_bytes_per_step": bn.sel_alg_bytes,
+               "GBps": round(bn.sel_alg_bytes / (ms_sel * 1e-3) / 1e9, 1),
+               "speedup_over_full_decode": round(ms / ms_sel, 3)}
     n_q, n_k, n_v, d_k, d_v = bn.shape
     gbs = bn.alg_bytes_step / (ms * 1e-3) / 1e9
     split_gbs = bn.alg_bytes_split / (split_ms * 1e-3) / 1e9
     rec = {"us_per_step": round(ms * 1e3, 2), "GBps": round(gbs, 1),
            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-           "us_per_step_spread": bn.step_pct_us,
+           "us_per_step_spread": spread,
            "alg_bytes_per_step": bn.alg_bytes_step,
            "split_us": round(split_ms * 1e3, 2), "combine_us": round(comb_ms * 1e3, 2),
            "split_GBps": round(split_gbs, 1),
@@ -463,6 +474,8 @@ def decode_record(name: str, steps: int, warmup: int, chunk: int = 0) -> dict:
                      "n_q": n_q, "n_k": n_k, "n_v": n_v, "d_k": d_k, "d_v": d_v},
            "chunk_rows": bn.S, "cache_replicas": bn.replicas,
            "timing": "hip graph replay" if graphed else "eager launches"}
+    if sel is not None:
+        rec["selective_v"] = sel
     bn.free()
     del bn
     return rec
@@ -931,7 +944,8 @@ def main():
                 if name == args.workload:
                     continue
                 log(f"workload {name}")
-                recs[name] = decode_record(name, args.steps, args.warmup, args.chunk)
+                recs[name] = decode_record(name, args.steps, args.warmup, args.chunk,
+                                           args.selective_k)
                 log(f"  step {recs[name]['us_per_step']} us, split {recs[name]['split_us']} us")
             sym = recs.get("decode64k_sym")
             for name in ("decode64k_dk64", "decode64k_dk128"):
