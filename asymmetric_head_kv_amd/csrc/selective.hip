@@ -213,6 +213,20 @@ __device__ void block_compact(KeyF key, int n, Threshold th, int* red, EmitF emi
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// lanes within each row of 16 (lanes without a source add 0), then lane 15
+// of each row added to the next row and lane 31 to rows 2 and 3.  All lanes
+// must be active.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // Register-resident variants for up to NT * E keys (NT threads): wave w,
 // lane l holds elements w * 64 E + 64 e + l (e < E) in its registers, so
 // each wave owns a contiguous segment and every load of a wave is 64
@@ -225,13 +239,17 @@ __device__ __forceinline__ int reg_index(int e) {
 }
 
 // hist: three kBins-word histograms (one per digit pass), zeroed and made
-// visible by a barrier before the call; red: 2 NT/64 ints.  Ends early as
-// the block variant.
+// visible by a barrier before the call; red: NT/64 ints, which other waves
+// may still read when a wave returns (the caller syncs before rewriting
+// them).  Two barriers per pass: after the histogram, and after the waves'
+// bin totals; every wave then finds the digit itself from the totals and
+// the bins of the wave that holds the krem-th key, so all waves take the
+// same exits.  Ends early as the block variant.
 template <int E, int NT = kSelThreads>
 __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k,
                                           uint32_t* hist, int* red) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x;
+  constexpr int NW = NT / 64, BPT = kBins / NT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
 #pragma unroll 1
@@ -244,38 +262,63 @@ __device__ Threshold reg_select_threshold(const uint32_t (&key)[E], int n, int k
       if (reg_index<E>(e) < n && (key[e] & pmask) == prefix)
         atomicAdd(&h[(key[e] >> shift) & dmask], 1u);
     __syncthreads();
-    constexpr int BPT = kBins / NT;
-    int cnt[BPT], own = 0;
+    // Thread t owns bins kBins-1-BPT t down to kBins-BPT-BPT t (descending
+    // across the block); a wave's total goes to red[wave].
+    int own = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) own += (int)h[kBins - 1 - BPT * tid - e];
+    own = wave_inclusive_scan(own);
+    if (lane == 63) red[wave] = own;
+    __syncthreads();
+    int tot[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot[w] = red[w];
+    // The wave ws whose bins hold the krem-th key from the top, and the
+    // keys in higher waves' bins.
+    int ws = NW - 1, above = 0, run = 0;
+    bool found = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const bool here = !found && run + tot[w] >= krem;
+      ws = here ? w : ws;
+      above = here ? run : above;
+      found = found || here;
+      run += tot[w];
+    }
+    // Lane l takes the bins of thread 64 ws + l.
+    const int t2 = 64 * ws + lane;
+    int cnt[BPT], mine = 0;
 #pragma unroll
     for (int e = 0; e < BPT; ++e) {
-      cnt[e] = (int)h[kBins - 1 - BPT * tid - e];
-      own += cnt[e];
+      cnt[e] = (int)h[kBins - 1 - BPT * t2 - e];
+      mine += cnt[e];
     }
-    int total;
-    const int above = block_exclusive_scan<NT>(own, red, &total);
-    if (above < krem && krem <= above + own) {
-      int run = above;
+    const int before = above + wave_inclusive_scan(mine) - mine;
+    const bool holds = before < krem && krem <= before + mine;
+    int digit = 0, kr = 0, whole = 0;
+    if (holds) {
+      int r = before;
 #pragma unroll
       for (int e = 0; e < BPT; ++e) {
-        if (run + cnt[e] >= krem) {
-          red[NW] = kBins - 1 - BPT * tid - e;
-          red[NW + 1] = krem - run;
-          red[NW + 2] = cnt[e] == krem - run;
+        if (r + cnt[e] >= krem) {
+          digit = kBins - 1 - BPT * t2 - e;
+          kr = krem - r;
+          whole = cnt[e] == kr;
           break;
         }
-        run += cnt[e];
+        r += cnt[e];
       }
     }
-    __syncthreads();
-    prefix |= (uint32_t)red[NW] << shift;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(holds);
+    const int src = bal != 0ull ? (int)__builtin_ctzll(bal) : 0;
+    digit = __builtin_amdgcn_readlane(digit, src);
+    kr = __builtin_amdgcn_readlane(kr, src);
+    whole = __builtin_amdgcn_readlane(whole, src);
+    prefix |= (uint32_t)digit << shift;
     pmask |= dmask << shift;
-    krem = red[NW + 1];
-    if (red[NW + 2] != 0 && prefix != 0u) {  // the whole bin is taken (as above)
-      __syncthreads();
-      return Threshold{prefix - 1u, 0};
-    }
+    krem = kr;
+    if (whole != 0 && prefix != 0u) return Threshold{prefix - 1u, 0};  // whole bin taken
   }
-  __syncthreads();
   return Threshold{prefix, krem};
 }
 
@@ -286,7 +329,8 @@ __device__ __forceinline__ void clear_hists(uint32_t* hist) {
 }
 
 // emit(pos, e) for every selected register slot e, pos = rank in index order
-// (NT threads; red: 2 NT/64 ints).
+// (NT threads; red: 2 NT/64 ints not used by the threshold search that
+// gave th, and not rewritten before the caller's next barrier).
 template <int E, int NT = kSelThreads, class EmitF>
 __device__ __forceinline__ void reg_compact(const uint32_t (&key)[E], int n, Threshold th,
                                             int* red, EmitF emit) {
@@ -309,7 +353,6 @@ __device__ __forceinline__ void reg_compact(const uint32_t (&key)[E], int n, Thr
     gt_before += red[w];
     eq_before += red[NW + w];
   }
-  __syncthreads();
   int pos0 = gt_before + min(eq_before, th.need_eq);
   const uint64_t below = lanes_below();
 #pragma unroll
@@ -501,7 +544,7 @@ __global__ __launch_bounds__(NT) void sel_local_kernel(
   constexpr int E = RS / NT;  // keys per thread
   constexpr int NW = NT / 64;
   __shared__ __align__(16) uint32_t hist[3 * kBins];
-  __shared__ int red[2 * NW];
+  __shared__ int red[4 * NW];
   __shared__ float wm[NW], wl[NW];
   const int rg = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -572,7 +615,7 @@ __global__ __launch_bounds__(NT) void sel_local_kernel(
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = order_key(s[e]);
   const Threshold th = reg_select_threshold<E, NT>(key, rows, top_k, hist, red);
-  reg_compact<E, NT>(key, rows, th, red, [&](int pos, int e) {
+  reg_compact<E, NT>(key, rows, th, red + 2 * NW, [&](int pos, int e) {
     if (pos < top_k) {
       cs[pos] = s[e];
       ci[pos] = j0 + reg_index<E>(e);
@@ -595,7 +638,7 @@ __global__ __launch_bounds__(NT) void sel_gather_kernel(
   constexpr int RPP = NT / LPR;               // V rows per pass of the block
   constexpr int U = 128 / RPP < 1 ? 1 : (128 / RPP > 8 ? 8 : 128 / RPP);  // passes in flight
   __shared__ __align__(16) uint32_t hist[3 * kBins];
-  __shared__ int red[2 * (NT / 64)];
+  __shared__ int red[4 * (NT / 64)];
   __shared__ int32_t sel_j[kMaxTopK];
   __shared__ float sel_w[kMaxTopK];
   __shared__ float part[RPP][DV + 4];
@@ -678,7 +721,7 @@ __global__ __launch_bounds__(NT) void sel_gather_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) key[e] = order_key(s[e]);
       const Threshold th = reg_select_threshold<E, NT>(key, n_c, kk, hist, red);
-      reg_compact<E, NT>(key, n_c, th, red, take);
+      reg_compact<E, NT>(key, n_c, th, red + 2 * (NT / 64), take);
     }
   } else {  // more candidates than registers hold: passes over global memory
     auto take = [&](int pos, int p) {
@@ -711,7 +754,7 @@ __global__ __launch_bounds__(NT) void sel_gather_kernel(
       w[u] = 0.f;
       v[u] = u32x4{0u, 0u, 0u, 0u};
       if (r < kk) {
-        const int j = sel_j[r];
+        const int j = min(max(sel_j[r], 0), L - 1);  // a chosen row is always in [0, L)
         w[u] = sel_w[r];
         v[u] = (fused && j == L - 1)
                    ? load16(vn + vl * EPL)
