@@ -12,15 +12,18 @@
 // the same K rows (the first wave to touch a row brings it from HBM, the
 // others hit the CU's L1 / the XCD's L2).  Each wave walks its chunk in tiles
 // of 64 rows:
-//   * all K and V loads of the tile are issued at once (16-byte lane loads,
-//     1 KiB contiguous per wave instruction);
+//   * all V loads of the tile are issued at once (16-byte lane loads, 1 KiB
+//     contiguous per wave instruction), K with them (paged caches) or one
+//     tile ahead, during the previous tile's V work (contiguous caches);
 //   * scores: each lane multiplies its 16-byte slice of a K row with the
 //     matching slice of q (bf16: packed two-element dot products), DPP sums
 //     over the lanes of a row; each lane keeps the score of exactly one row
 //     of the tile;
 //   * online softmax over tiles (running max m, running sum l, rescaled
-//     accumulator), max / sum by wave reductions, base-2 exponentials with
-//     log2(e) folded into the query scale;
+//     accumulator) with base-2 exponentials, log2(e) folded into the query
+//     scale; m moves only when a score passes it by more than 8 (log2
+//     units), so most tiles skip the wave max, and l is summed per lane and
+//     reduced once per chunk;
 //   * V rows are accumulated in fp32 with each lane owning a 16-byte column
 //     slice; the row's probability arrives by ds_bpermute from the lane that
 //     owns it (bf16: two rows per step, their probabilities packed as a bf16
@@ -181,27 +184,49 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   };
   size_t page_next = PAGED ? page_of(0) : 0;
 
-  // One tile of 64 rows per iteration: all of its K loads and the first VB
-  // V loads are issued together and the scores wait only for K.  (Keeping a
-  // second tile's loads in flight -- double buffers, or re-filling each
-  // register right after use -- costs occupancy and measured slower.)
+  // One tile of 64 rows per iteration: its V loads go out at the top and the
+  // scores use K rows requested earlier.  Contiguous caches request the next
+  // tile's K rows right after this tile's scores, while the softmax and the
+  // V products run (32k step 28.9 -> 28.2 us, ragged batch -0.5%, 4 x 64k
+  // +0.6%); paged caches request K together with V, the tile's page read one
+  // tile ahead, and so do fp32 caches (their wide K tiles would spill).
+  // (Keeping a whole second tile in flight -- double buffers, or re-filling
+  // each register right after use -- measured slower: more bytes in flight
+  // per wave lower the achieved HBM rate here.)
+  constexpr bool kNextK = !PAGED && kDot;
+  u32x4 kv[NK];
+  auto issue_k = [&](int t0, const T* kt) {
+    if (t0 + kTile <= rows) {
+#pragma unroll
+      for (int u = 0; u < NK; ++u) kv[u] = load16(kt + (size_t)(u * RPL_K + kr) * DK);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NK; ++u) kv[u] = load_k(t0 + u * RPL_K + kr, kt, t0);
+    }
+  };
+  if constexpr (kNextK) issue_k(0, k_tile(kc, 0, 0));
+  // Per-lane row sums: the wave sum is taken once, after the last tile.
+  float l_lane[H];
+#pragma unroll
+  for (int hh = 0; hh < H; ++hh) l_lane[hh] = 0.f;
+
   for (int t0 = 0; t0 < rows; t0 += kTile) {
     const size_t page = page_next;
     if constexpr (PAGED) page_next = t0 + kTile < rows ? page_of(t0 + kTile) : 0;
     const T* kt = k_tile(kc, t0, page);
     const T* vt = v_tile(vc, t0, page);
-    u32x4 kv[NK], vv[VB];
+    u32x4 vv[VB];
+    if constexpr (!kNextK) issue_k(t0, kt);
     if (t0 + kTile <= rows) {
-#pragma unroll
-      for (int u = 0; u < NK; ++u) kv[u] = load16(kt + (size_t)(u * RPL_K + kr) * DK);
 #pragma unroll
       for (int u = 0; u < VB; ++u) vv[u] = load16_nt(vt + (size_t)(u * RPL_V + vr) * DV);
     } else {
 #pragma unroll
-      for (int u = 0; u < NK; ++u) kv[u] = load_k(t0 + u * RPL_K + kr, kt, t0);
-#pragma unroll
       for (int u = 0; u < VB; ++u) vv[u] = load_v(t0 + u * RPL_V + vr, vt, t0);
     }
+    // Every load of the tile is issued before any arithmetic: left alone, the
+    // scheduler sinks each K load to its dot product and waits for it there.
+    __builtin_amdgcn_sched_barrier(0);
 
     // Scores (one row per lane per head) and the online-softmax update.
     float s_mine[H];
@@ -225,21 +250,33 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         s_mine[hh] = (u == kl) ? s : s_mine[hh];
       }
     }
+    if constexpr (kNextK) {
+      if (t0 + kTile < rows) issue_k(t0 + kTile, k_tile(kc, t0 + kTile, 0));
+    }
     if constexpr (kDot) {
 #pragma unroll
       for (int hh = 0; hh < H; ++hh) s_mine[hh] *= qscale;
     }
+    // Online softmax with a lazily moved reference: the running max m_run is
+    // raised (and l, acc rescaled) only when some score of the tile exceeds
+    // it by more than 8 in log2 units, so the weights 2^(s - m_run) stay
+    // below 2^8 and most tiles need no wave reduction.  The partial's m is
+    // then at most 8 below the chunk's true max; the combine's merge is exact
+    // for any such reference.  The first tile always sets it (m_run = -inf).
     float p[H];
 #pragma unroll
     for (int hh = 0; hh < H; ++hh) {
       if (t0 + my_row >= rows) s_mine[hh] = -INFINITY;
-      const float m_new = fmaxf(m_run[hh], wave_max(s_mine[hh]));
-      p[hh] = fast_exp2(s_mine[hh] - m_new);
-      const float alpha = fast_exp2(m_run[hh] - m_new);
-      l_run[hh] = l_run[hh] * alpha + wave_sum(p[hh]);
-      m_run[hh] = m_new;
+      if (__any(s_mine[hh] > m_run[hh] + 8.f)) {
+        const float m_new = fmaxf(m_run[hh], wave_max(s_mine[hh]));
+        const float alpha = fast_exp2(m_run[hh] - m_new);
+        l_lane[hh] *= alpha;
+        m_run[hh] = m_new;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
+        for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
+      }
+      p[hh] = fast_exp2(s_mine[hh] - m_run[hh]);
+      l_lane[hh] += p[hh];
     }
 
     // bf16: pack this lane's probability with that of row my_row ^ RPL_V
@@ -301,6 +338,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
   // Sum the row groups of the wave (lanes with equal vl) and write each
   // head's partial.
+#pragma unroll
+  for (int hh = 0; hh < H; ++hh) l_run[hh] = wave_sum(l_lane[hh]);
 #pragma unroll
   for (int hh = 0; hh < H; ++hh) {
 #pragma unroll
