@@ -53,7 +53,7 @@ constexpr int kTile = 64;  // rows per wave iteration: one score per lane
 // pm.table[b][j / page_rows] (see PageMap).  Pages hold a multiple of 64 rows
 // and chunks start at multiples of 64, so a 64-row tile never straddles two
 // pages: one table entry per tile, read one tile ahead.
-template <typename T, int DK, int DV, int H, bool PAGED>
+template <typename T, int DK, int DV, int H, bool PAGED, bool NEXT_K>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const T* __restrict__ q, const T* kc, const T* vc,
     const int32_t* __restrict__ ctx_len, float* __restrict__ part_ml,
@@ -185,15 +185,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   size_t page_next = PAGED ? page_of(0) : 0;
 
   // One tile of 64 rows per iteration: its V loads go out at the top and the
-  // scores use K rows requested earlier.  Contiguous caches request the next
-  // tile's K rows right after this tile's scores, while the softmax and the
-  // V products run (32k step 28.9 -> 28.2 us, ragged batch -0.5%, 4 x 64k
-  // +0.6%); paged caches request K together with V, the tile's page read one
-  // tile ahead, and so do fp32 caches (their wide K tiles would spill).
-  // (Keeping a whole second tile in flight -- double buffers, or re-filling
-  // each register right after use -- measured slower: more bytes in flight
-  // per wave lower the achieved HBM rate here.)
-  constexpr bool kNextK = !PAGED && kDot;
+  // scores use K rows requested earlier.  With NEXT_K (bf16 contiguous
+  // caches, chosen by the launcher) the next tile's K rows are requested
+  // right after this tile's scores, while the softmax and the V products run;
+  // otherwise K goes out together with V (paged caches read the tile's page
+  // one tile ahead).  (Keeping a whole second tile in flight -- double
+  // buffers, or re-filling each register right after use -- measured slower:
+  // more bytes in flight per wave lower the achieved HBM rate here.)
+  static_assert(!NEXT_K || (!PAGED && kDot), "K look-ahead: bf16, contiguous");
+  constexpr bool kNextK = NEXT_K;
   u32x4 kv[NK];
   auto issue_k = [&](int t0, const T* kt) {
     if (t0 + kTile <= rows) {
@@ -483,14 +483,33 @@ static int heads_per_wave(const DecodeArgs& a) {
   return (a.n_q == 2 * a.n_v && (a.n_q / a.n_k) % 2 == 0) ? 2 : 1;
 }
 
-template <typename T, int DK, int DV, int H, bool PAGED>
+template <typename T, int DK, int DV, int H, bool PAGED, bool NEXT_K = false>
 static void launch_split_hp(const DecodeArgs& a) {
   dim3 grid(a.C, (a.n_q + 4 * H - 1) / (4 * H), a.batch);
-  hipLaunchKernelGGL((decode_split_kernel<T, DK, DV, H, PAGED>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((decode_split_kernel<T, DK, DV, H, PAGED, NEXT_K>), grid, dim3(256), 0,
+                     a.stream,
                      (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.ctx_len,
                      a.part_ml, a.part_acc, a.n_q, a.n_k, a.n_v, a.l_cap, a.max_ctx, a.S, a.C,
                      a.scale * kLog2e, (const T*)a.k_new, (const T*)a.v_new, (T*)a.k_cache,
                      (T*)a.v_cache, a.pages);
+}
+
+// Contiguous bf16 caches with the K look-ahead (same-process A/B, µs per
+// step, without -> with): at d_k <= 64 always (32k 28.9 -> 28.2, 16 ragged
+// sequences 235.2 -> 233.9; 4 x 64k 181.0 -> 175.6 against the form without
+// it -- 174.5 before the lazy reference), at larger d_k for chunks of up to
+// 1024 rows (32k symmetric d = 128: 50.3 -> 48.3) but not for longer ones
+// (4 x 64k, d_k = 128: 198.3 against 202.4; symmetric 64k alike).
+template <typename T, int DK, int DV, int H>
+static void launch_split_contig(const DecodeArgs& a) {
+  if constexpr (sizeof(T) == 2 && DK <= 64) {
+    launch_split_hp<T, DK, DV, H, false, true>(a);
+  } else if constexpr (sizeof(T) == 2) {
+    if (a.S <= 1024) launch_split_hp<T, DK, DV, H, false, true>(a);
+    else launch_split_hp<T, DK, DV, H, false>(a);
+  } else {
+    launch_split_hp<T, DK, DV, H, false>(a);
+  }
 }
 
 template <typename T, int DK, int DV>
@@ -498,10 +517,10 @@ static hipError_t launch_split_t(const DecodeArgs& a) {
   const bool paged = a.pages.table != nullptr;
   if (heads_per_wave(a) == 2) {
     if (paged) launch_split_hp<T, DK, DV, 2, true>(a);
-    else launch_split_hp<T, DK, DV, 2, false>(a);
+    else launch_split_contig<T, DK, DV, 2>(a);
   } else {
     if (paged) launch_split_hp<T, DK, DV, 1, true>(a);
-    else launch_split_hp<T, DK, DV, 1, false>(a);
+    else launch_split_contig<T, DK, DV, 1>(a);
   }
   return hipGetLastError();
 }
