@@ -88,8 +88,11 @@ int32_t diffqkv_decode_chunk(int32_t n_q, int32_t n_k, int32_t n_v,
  * Workspace bytes diffqkv_decode needs for these sizes and chunk length
  * (chunk_tokens = 0: the automatic choices of both diffqkv_decode and
  * diffqkv_decode_paged, whichever needs more).  The workspace holds the
- * per-chunk partial results (running max, sum and weighted V sum, fp32) of
- * the split step.  Pure host computation.
+ * per-chunk partial results of the split step, fp32: a reference m (within
+ * 8 log2 units below the chunk's largest scaled score, so the chunk's
+ * weights 2^(s - m) stay below 2^8), the sum l of those weights and the
+ * weighted V sum; the combine merges them exactly for any such m.  Their
+ * layout is internal.  Pure host computation.
  */
 int32_t diffqkv_decode_workspace(int32_t n_q, int32_t n_k, int32_t n_v,
                                  int32_t d_k, int32_t d_v, int32_t batch,
@@ -192,7 +195,7 @@ int32_t diffqkv_decode_append_noalloc(int32_t n_q, int32_t n_k, int32_t n_v, int
  * split and combine kernels of FlexHeadFA separately.  Arguments have the
  * meaning given above; both calls of one step must pass the same sizes,
  * chunk_tokens and workspace.  The split kernel writes every non-empty
- * chunk's (max, sum, weighted V sum) to the workspace; the combine reads
+ * chunk's (reference m, sum, weighted V sum) to the workspace; the combine reads
  * them and writes out and lse.  k_cache / v_cache are written only when
  * k_new / v_new are given (both or neither).
  */
