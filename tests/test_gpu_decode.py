@@ -93,6 +93,57 @@ def test_decode_logits_far_above_the_rest(dtype):
         assert_lse_close(lse, ref_lse, dtype, f"spiked decode chunk={chunk}")
 
 
+def _log2_score_rows(case, level):
+    """Set every K row so that its (scaled, log2-unit) logit against an
+    all-ones q is level[j] (d_k equal elements per row)."""
+    d_k = case.d_k
+    c = np.asarray(level, dtype=np.float64) / (np.log2(np.e) * case.scale * d_k)
+    row = np.repeat(c[:, None], d_k, axis=1).astype(np.float32)
+    if case.dtype == "bf16":
+        case.q[...] = 0x3F80
+        row = synth.f32_to_bf16_bits(row)
+    else:
+        case.q[...] = 1.0
+    case.k_cache[:, :, : len(level), :] = row[None, None]
+
+
+@pytest.mark.parametrize("jump", [7.9, 8.1])
+@pytest.mark.parametrize("chunk", [128, 512])
+def test_decode_logits_step_up_after_first_tile(jump, chunk):
+    # Every chunk's first 64-row tile has logits near 0 (log2 units), the
+    # rest lie `jump` higher.  Below the kernel's margin of 8 the chunk keeps
+    # the first tile's reference and its weights stay just under 2^8 over
+    # every later tile; above it the reference moves once per chunk.
+    case = synth.make_case(612, dtype="bf16", batch=1, n_q=16, n_k=4, n_v=16, d_k=64,
+                           d_v=128, ctx_len=[2000], l_cap=2048, poison_tail=True)
+    j = np.arange(2000)
+    _log2_score_rows(case, np.where(j % chunk < 64, 0.0, jump) + 0.01 * (j % 7))
+    ref, ref_lse = oracle_decode(case)
+    _say("decode logits step up", jump, "chunk", chunk)
+    got, lse = run_decode(case, chunk=chunk)
+    assert np.isfinite(got).all()
+    assert_close(got, ref, "bf16", f"step-up decode jump={jump} chunk={chunk}")
+    assert_lse_close(lse, ref_lse, "bf16", f"step-up decode jump={jump} chunk={chunk}")
+
+
+@pytest.mark.parametrize("slope", [7.9 / 64, 8.1 / 64, 0.5])
+def test_decode_logits_rising_ramp_f32(slope):
+    # fp32 cache, logits rising by `slope` (log2 units) per row over 3000
+    # rows up to 0 at the last one (from -1500 at most, so lse stays small
+    # enough for its absolute tolerance): the running reference lags the
+    # maximum by up to the margin, or moves on every tile.
+    case = synth.make_case(613, dtype="f32", batch=1, n_q=8, n_k=2, n_v=8, d_k=32, d_v=64,
+                           ctx_len=[3000], l_cap=3072, poison_tail=True)
+    _log2_score_rows(case, slope * (np.arange(3000) - 2999))
+    ref, ref_lse = oracle_decode(case)
+    for chunk in (0, 256):
+        _say("decode rising ramp f32", slope, "chunk", chunk)
+        got, lse = run_decode(case, chunk=chunk)
+        assert np.isfinite(got).all()
+        assert_close(got, ref, "f32", f"ramp decode slope={slope} chunk={chunk}")
+        assert_lse_close(lse, ref_lse, "f32", f"ramp decode slope={slope} chunk={chunk}")
+
+
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-{c[4]}x{c[5]}")
 def test_decode_small_matches_oracle(cfg):
     dtype, n_q, n_k, n_v, d_k, d_v, lens, cap = cfg
