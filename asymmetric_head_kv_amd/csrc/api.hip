@@ -44,6 +44,16 @@ constexpr int kMaxChunks = 8192;      // bounds the workspace and the combine's 
 constexpr int kRaggedBatch = 8;
 constexpr int kRaggedOversub = 7;
 constexpr int kMinChunk = 64;
+// Contiguous layouts with d_k <= 64 (split kernel with the K look-ahead)
+// whose one-round plan gives chunks of kLongChunk rows or more aim at 15/16
+// of the CUs instead, chunks rounded up to kLongRound rows: fewer, longer
+// streams run faster there (4 x 64k, 16 / 4 / 16 heads: 4096-row chunks
+// 175.8 us per step, 4416 173.5, 4608 171.9 -- the rule's choice, 15 chunks
+// per sequence -- and 5120 172.4; same process, three boxes).  Without the
+// look-ahead fewer workgroups were slower (d_k 128: 5120-row chunks 227 us
+// against 198.6 at 4096; the symmetric layout 322.6 against 319.8).
+constexpr int kLongChunk = 4096;
+constexpr int kLongRound = 512;
 
 bool is_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
@@ -68,17 +78,24 @@ int to_status(hipError_t e) { return e == hipSuccess ? DQKV_OK : DQKV_ERR_HIP; }
 // give every CU about the planned waves (times kRaggedOversub for large
 // batches), in multiples of 64 rows.  H = query heads per wave; small =
 // fewer than kSmallTileElems per workgroup tile.
-int plan_chunk_h(int n_q, int H, int batch, int max_ctx, bool paged, bool small) {
+int plan_chunk_h(int n_q, int H, int batch, int max_ctx, bool paged, bool small,
+                 bool look_ahead) {
   long long quads = (long long)batch * ((n_q / H + 3) / 4);
   if (quads < 1) quads = 1;  // an empty batch launches nothing
-  const int waves =
-      (paged || small || batch >= kRaggedBatch) ? kWavesPerCUPaged : kWavesPerCUContig;
+  const bool one_round = !(paged || small || batch >= kRaggedBatch);
+  const int waves = one_round ? kWavesPerCUContig : kWavesPerCUPaged;
   const long long want_wg = (long long)kCUs * waves / 4 *
                             (batch >= kRaggedBatch ? kRaggedOversub : 1);
   long long chunks_per_seq = (want_wg + quads - 1) / quads;
   if (chunks_per_seq < 1) chunks_per_seq = 1;
   long long S = (max_ctx + chunks_per_seq - 1) / chunks_per_seq;
   S = (S + kMinChunk - 1) / kMinChunk * kMinChunk;
+  if (one_round && look_ahead && S >= kLongChunk) {
+    long long cps = (want_wg * 15 / 16 + quads - 1) / quads;
+    if (cps < 1) cps = 1;
+    S = (max_ctx + cps - 1) / cps;
+    S = (S + kLongRound - 1) / kLongRound * kLongRound;
+  }
   if (S < kMinChunk) S = kMinChunk;
   const long long s_floor = ((long long)max_ctx + kMaxChunks - 1) / kMaxChunks;
   if (S < s_floor) S = (s_floor + kMinChunk - 1) / kMinChunk * kMinChunk;
@@ -96,7 +113,7 @@ int plan_chunk(int n_q, int n_k, int n_v, int d_k, int d_v, int batch, int max_c
   const long long heads = 4LL * H, G = n_q / n_k, Gv = n_q / n_v;
   const long long k_heads = (heads + G - 1) / G, v_heads = (heads + Gv - 1) / Gv;
   const long long tile = 64LL * (k_heads * d_k + v_heads * d_v);
-  return plan_chunk_h(n_q, H, batch, max_ctx, paged, tile < kSmallTileElems);
+  return plan_chunk_h(n_q, H, batch, max_ctx, paged, tile < kSmallTileElems, d_k <= 64);
 }
 
 int chunks_for(int max_ctx, int S) {

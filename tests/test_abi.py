@@ -106,7 +106,7 @@ def test_workspace_and_chunk_plan(lib):
     # workspace query covers both.
     for (B, n_q, d_v, ctx, S_contig, S_paged) in [(1, 16, 128, 32768, 512, 256),
                                                   (16, 16, 128, 32769, 640, 640),
-                                                  (4, 16, 128, 65536, 4096, 2048),
+                                                  (4, 16, 128, 65536, 4608, 2048),
                                                   (1, 4, 64, 256, 64, 64)]:
         S = dq.decode_chunk(n_q, 4 if n_q > 4 else 1, n_q, 64, d_v, B, ctx)
         assert S == S_contig
@@ -118,6 +118,12 @@ def test_workspace_and_chunk_plan(lib):
     # chunks).  Large batches (lengths unknown to the host, possibly ragged)
     # plan about seven times more chunks than a small batch would.
     assert 32768 // dq.decode_chunk(16, 4, 16, 64, 128, 1, 32768) == 64
+    # One-round plans with chunks of 4096+ rows aim at 15/16 of the CUs in
+    # 512-row steps when d_k <= 64 (4 x 64k: 15 chunks of 4608 rows), and keep
+    # one workgroup per CU at larger d_k.
+    assert dq.decode_chunk(16, 4, 16, 64, 128, 4, 65536) == 4608
+    assert dq.decode_chunk(16, 4, 16, 128, 128, 4, 65536) == 4096
+    assert dq.decode_chunk(16, 16, 16, 128, 128, 4, 65536) == 4096
     assert -(-32769 // dq.decode_chunk(16, 4, 16, 64, 128, 16, 32769)) >= 32
     # Layouts whose four-wave workgroup loads under 24Ki elements per 64-row
     # tile plan two workgroups per CU: the pages' SIGMA-1.5B attention (32 /
