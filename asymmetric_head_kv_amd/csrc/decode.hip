@@ -13,8 +13,9 @@
 // others hit the CU's L1 / the XCD's L2).  Each wave walks its chunk in tiles
 // of 64 rows:
 //   * all V loads of the tile are issued at once (16-byte lane loads, 1 KiB
-//     contiguous per wave instruction), K with them (paged caches) or one
-//     tile ahead, during the previous tile's V work (contiguous caches);
+//     contiguous per wave instruction), K either with them or one tile
+//     ahead, during the previous tile's V work (bf16 contiguous caches with
+//     d_k <= 64 or chunks of at most 1024 rows; see the launcher);
 //   * scores: each lane multiplies its 16-byte slice of a K row with the
 //     matching slice of q (bf16: packed two-element dot products), DPP sums
 //     over the lanes of a row; each lane keeps the score of exactly one row
